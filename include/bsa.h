@@ -1,0 +1,165 @@
+/*
+ * bsa.h -- C ABI of the MI355X (gfx950) Block Sparse Attention library (libbsa.so).
+ *
+ * Block Sparse Attention over a 3D video latent grid, as the LongCat-Video pages describe it:
+ *   - the visual tokens of a (T, H, W) latent grid are cut into small 3D cubes, and each query
+ *     cube attends only to the few key cubes most relevant to it, chosen by similarity rather
+ *     than distance, which keeps attention compute under about a tenth of dense
+ *     ["LongCat-Video : Generate 1 minute long AI videos with this model" (Data Science in Your
+ *     Pocket), section "Sparse attention"; "LongCat-Video视频生成模型发布 迈出世界模型探索第一步"
+ *     (youleyou), section "块稀疏注意力（BSA）"];
+ *   - a query cube always keeps its own cube and skips every unselected block pair entirely
+ *     ["LongCat-Video deep dive" (ai-news-5min-kr), block-sparse attention paragraph and its
+ *     same-table analogy];
+ *   - block-causal attention with cached condition-frame K/V serves video continuation
+ *     ["LongCat-Video 高效長視頻生成探索世界模型的第壹步" (meituan.com talk), section 2.1;
+ *     youleyou page, section "长视频生成：5分钟连贯输出，质量全程在线"; Data Science in Your
+ *     Pocket page, section "The core idea: one model for all video tasks"];
+ *   - forward and backward both exist, for inference and training (meituan.com talk, section 2.2).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  Layout.  Token tensors are [B, N, Hh, D], C-contiguous ("BNHD"), tokens in raster order of the
+ *    latent grid: token n = (t*H + h)*W + w.  Query, key and value tensors (q, k, v, o, d_o and the
+ *    gradients) hold only the NOISE segment, i.e. the last T - cond_T frames, so N = Nq =
+ *    (T - cond_T)*H*W.  k_cache / v_cache hold the first cond_T frames: N = Nc = cond_T*H*W.
+ *  Cubes.  A cube is ct x ch x cw tokens (c = ct*ch*cw).  Cube coordinates (a, b, e) =
+ *    (t/ct, h/ch, w/cw) inside a segment; the cube id inside a segment is (a*(H/ch) + b)*(W/cw) + e.
+ *    Key cube ids put the nbc condition cubes first (0..nbc-1) and the nbq noise cubes after them
+ *    (nbc..nbc+nbq-1); query cube i is key cube nbc+i.  nbk = nbc + nbq.
+ *  Pooled tensors are [B, Hh, nbq, D] fp32.  idx is [B, Hh, nbq, k_sel] int32, each row ascending.
+ *    mask is [B, Hh, nbq, nbk] uint8 (1 = key cube attended).  lse is [B, Hh, Nq] fp32 (natural log).
+ *  Ownership.  The caller owns every buffer; the library never allocates, frees or synchronises.
+ *    Device pointers must be device-resident (hipMalloc / torch) and 16-byte aligned.
+ *  Streams.  Every launch is asynchronous on the stream passed in (NULL = the null stream).
+ *  Errors.  Arguments are checked on the host before any launch and before any HIP call; a bad
+ *    argument returns an error code and launches nothing.  A launch failure returns BSA_ERR_HIP.
+ *    Faults inside kernels surface, as usual for HIP, at the caller's next synchronisation.
+ *    No C++ exception crosses this interface.
+ *  Threads.  The library keeps no per-call state; concurrent calls on different streams are safe
+ *    as long as their output and workspace buffers do not overlap.
+ */
+#ifndef BSA_H_
+#define BSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  BSA_OK = 0,
+  BSA_ERR_INVALID_ARG = 1, /* null required pointer, non-positive size, k_sel mismatch, bad r  */
+  BSA_ERR_SHAPE = 2,       /* grid not divisible by the cube, cond_T not a cube multiple, ...   */
+  BSA_ERR_UNSUPPORTED = 3, /* head_dim or cube size outside what the kernels implement          */
+  BSA_ERR_WORKSPACE = 4,   /* workspace missing or smaller than bsa_workspace_bytes()           */
+  BSA_ERR_HIP = 5,         /* a HIP launch or runtime call failed                               */
+  BSA_ERR_INTERNAL = 6     /* unexpected internal failure (caught exception)                    */
+} bsa_status_t;
+
+typedef enum { BSA_F32 = 0, BSA_BF16 = 1 } bsa_dtype_t;
+
+/* Shape of one problem.  T counts all frames, condition frames included; cond_T = 0 means no
+ * condition cache and plain (non-causal) block-sparse attention.
+ * Requirements: all sizes > 0 except cond_T >= 0; head_dim in {64, 128}; T - cond_T, H and W
+ * divisible by cube_t, cube_h, cube_w; cond_T divisible by cube_t and cond_T < T;
+ * cube size c = cube_t*cube_h*cube_w <= 256. */
+typedef struct {
+  int32_t batch, heads, head_dim; /* B, Hh, D                                  */
+  int32_t T, H, W;                /* latent grid, condition frames included    */
+  int32_t cube_t, cube_h, cube_w; /* ct, ch, cw                                */
+  int32_t cond_T;                 /* leading condition frames (0 = none)       */
+} bsa_problem_t;
+
+/* Mean-pool every cube of one token tensor (3D cube partition plus per-cube mean; the relevance
+ * descriptor used to find the most similar cubes, Data Science in Your Pocket page, section
+ * "Sparse attention").
+ *   x       device, [B, Nq, Hh, D] of dtype (noise segment of Q or K)
+ *   x_mean  device, [B, Hh, nbq, D] fp32, written: x_mean[b,h,i,:] = (1/c) * sum of the c token
+ *           rows of cube i for head h, accumulated in fp32.
+ * Errors: INVALID_ARG (null pointer, bad sizes), SHAPE, UNSUPPORTED, HIP. */
+bsa_status_t bsa_block_pool(const bsa_problem_t* p, bsa_dtype_t dtype, const void* x,
+                            float* x_mean, hipStream_t stream);
+
+/* Score every candidate key cube against each query cube and keep the top r (top-r key blocks,
+ * youleyou page, section "块稀疏注意力（BSA）"; similarity-based choice, Data Science in Your Pocket
+ * page, section "Sparse attention"; own block always kept, ai-news-5min-kr deep dive, same-table
+ * analogy).
+ *   q_mean, k_mean  device, [B, Hh, nbq, D] fp32 (from bsa_block_pool on Q and on noise K)
+ *   r               >= 0; clamped to the nbq-1 candidates (r >= nbq-1 gives dense attention)
+ *   idx             device, [B, Hh, nbq, k_sel] int32, written; k_sel = bsa_num_selected(p, r)
+ *   mask            device, [B, Hh, nbq, nbk] uint8, written, or NULL to skip it
+ * Score S[i,j] = D^-1/2 * <q_mean_i, k_mean_j> in fp32.  Row i keeps the forced set (all nbc
+ * condition cubes and its own cube nbc+i) plus the first min(r, nbq-1) noise cubes j != i in order
+ * of (score descending, cube id ascending); -0.0 counts as +0.0.  Rows are written ascending.
+ * Scores must be finite.
+ * Errors: INVALID_ARG, SHAPE, UNSUPPORTED, HIP. */
+bsa_status_t bsa_select_topr(const bsa_problem_t* p, const float* q_mean, const float* k_mean,
+                             int32_t r, int32_t* idx, uint8_t* mask, hipStream_t stream);
+
+/* Gathered block-sparse flash attention, forward (skips unselected block pairs, ai-news-5min-kr
+ * deep dive, block-sparse attention paragraph).  For each query cube i:
+ *   O_i = softmax(softmax_scale * Q_i K_sel(i)^T) V_sel(i),  LSE_i = log sum exp(...)
+ * where K_sel(i)/V_sel(i) are the tokens of the key cubes in idx[b,h,i,:]; condition cubes
+ * (id < nbc) are read from k_cache / v_cache, noise cubes from k / v (block-causal continuation
+ * with a condition-token cache, meituan.com talk, section 2.1).
+ *   q, k, v            device, [B, Nq, Hh, D] dtype
+ *   k_cache, v_cache   device, [B, Nc, Hh, D] dtype; must be NULL iff cond_T == 0
+ *   idx, k_sel         as written by bsa_select_topr (every entry in [0, nbk), rows ascending)
+ *   o                  device, [B, Nq, Hh, D] dtype, written (bf16 by round-to-nearest-even)
+ *   lse                device, [B, Hh, Nq] fp32, written
+ *   ws, ws_bytes       device workspace of at least bsa_workspace_bytes(p, dtype, k_sel, 0)
+ *                      bytes (may be NULL when that is 0); contents are scratch
+ * Errors: INVALID_ARG, SHAPE, UNSUPPORTED, WORKSPACE, HIP. */
+bsa_status_t bsa_sparse_attn_fwd(const bsa_problem_t* p, bsa_dtype_t dtype, const void* q,
+                                 const void* k, const void* v, const void* k_cache,
+                                 const void* v_cache, const int32_t* idx, int32_t k_sel,
+                                 float softmax_scale, void* o, float* lse, void* ws,
+                                 size_t ws_bytes, hipStream_t stream);
+
+/* Backward of bsa_sparse_attn_fwd with the selection held constant (the forward and backward
+ * both ship, meituan.com talk, section 2.2).  With P = exp(scale*Q_i K_j^T - LSE_i):
+ *   dV_j += P^T dO_i;  dS = P o (dO_i V_j^T - Delta_i);  dQ_i += scale*dS K_j;
+ *   dK_j += scale*dS^T Q_i;  Delta_i = rowsum(dO_i o O_i),  over every i and j in idx[b,h,i,:].
+ *   q, k, v, o, d_o    device, [B, Nq, Hh, D] dtype (o, lse from the forward)
+ *   lse                device, [B, Hh, Nq] fp32
+ *   dq, dk, dv         device, [B, Nq, Hh, D] fp32, overwritten
+ *   ws, ws_bytes       device workspace of at least bsa_workspace_bytes(p, dtype, k_sel, 1)
+ * cond_T must be 0 (gradients of the condition cache are not produced): UNSUPPORTED otherwise.
+ * Errors: INVALID_ARG, SHAPE, UNSUPPORTED, WORKSPACE, HIP. */
+bsa_status_t bsa_sparse_attn_bwd(const bsa_problem_t* p, bsa_dtype_t dtype, const void* q,
+                                 const void* k, const void* v, const void* o, const void* d_o,
+                                 const float* lse, const int32_t* idx, int32_t k_sel,
+                                 float softmax_scale, float* dq, float* dk, float* dv, void* ws,
+                                 size_t ws_bytes, hipStream_t stream);
+
+/* ---- helpers (host only, no HIP calls) ---- */
+
+/* k_sel = nbc + 1 + min(r, nbq - 1), or -1 if p is invalid or r < 0. */
+int32_t bsa_num_selected(const bsa_problem_t* p, int32_t r);
+
+/* Workspace bytes for the forward (bwd = 0) or backward (bwd = 1) call; (size_t)-1 if invalid. */
+size_t bsa_workspace_bytes(const bsa_problem_t* p, bsa_dtype_t dtype, int32_t k_sel, int32_t bwd);
+
+/* Human-readable name of a status code (static string). */
+const char* bsa_status_string(bsa_status_t s);
+
+/* Text of the last argument error raised on this thread (static per thread, never NULL). */
+const char* bsa_last_error(void);
+
+/* Stage timing for profiling.  When events != NULL, every entry point records events[k] (HIP
+ * events created by the caller) on its stream at the boundaries of its internal kernels: slot 0
+ * before the first launch and slot s after internal stage s, for s < n.  Stage slots are listed
+ * by bsa_stage_name(); pass NULL to disable.  The setting is per host thread. */
+void bsa_set_stage_events(hipEvent_t* events, int32_t n);
+
+/* Name of internal stage s of the last entry point called on this thread ("" when none). */
+const char* bsa_stage_name(int32_t s);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* BSA_H_ */

@@ -1,0 +1,135 @@
+"""Pins for the oracle's backward (CPU only).
+
+Central finite differences of the oracle's forward on the 256-token tiny grid with the selection
+held fixed; torch float64 autograd through scaled_dot_product_attention (dense and token-masked);
+and the gradient invariants sum_k dV = sum_q dO, sum_k dK = 0, and
+sum_q <dQ, Q> = sum_k <dK, K>."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as orc
+from video_dit_block_cube_amd import synth
+
+
+def _tiny(seed_extra=0):
+    w = synth.workload(1)
+    x = synth.make_inputs(w)
+    p = orc.Problem(**w.shape_dict)
+    rng = np.random.default_rng(4242 + seed_extra)
+    dO = rng.standard_normal(x["q"].shape)
+    return p, {k: v.astype(np.float64) for k, v in x.items()}, dO, w
+
+
+def _loss(q, k, v, dO, idx, p, scale):
+    O, _ = orc.sparse_attn_fwd(q, k, v, None, None, idx, p, scale)
+    return float(np.sum(O * dO))
+
+
+def test_finite_differences_tiny_grid():
+    p, x, dO, w = _tiny()
+    scale = 1 / math.sqrt(p.head_dim)
+    qm, km = orc.block_pool(x["q"], p), orc.block_pool(x["k"], p)
+    idx, _ = orc.select_topr(qm, km, p, w.r)
+    grads = orc.attn_bwd(x["q"], x["k"], x["v"], dO, idx, p, scale)
+    rng = np.random.default_rng(77)
+    h = 1e-5
+    names = ("q", "k", "v")
+    # 32 random directions over all three inputs jointly
+    for _ in range(32):
+        dirs = [rng.standard_normal(x[n].shape) for n in names]
+        plus = [x[n] + h * d for n, d in zip(names, dirs)]
+        minus = [x[n] - h * d for n, d in zip(names, dirs)]
+        fd = (_loss(*plus, dO, idx, p, scale) - _loss(*minus, dO, idx, p, scale)) / (2 * h)
+        an = sum(float(np.sum(g * d)) for g, d in zip(grads, dirs))
+        assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (fd, an)
+    # 256 random coordinates (spread over q, k, v)
+    flat = [g.ravel() for g in grads]
+    for t in range(256):
+        which = t % 3
+        pos = int(rng.integers(0, x[names[which]].size))
+        args = [x[n].copy() for n in names]
+        args[which].ravel()[pos] += h
+        lp = _loss(*args, dO, idx, p, scale)
+        args[which].ravel()[pos] -= 2 * h
+        lm = _loss(*args, dO, idx, p, scale)
+        fd = (lp - lm) / (2 * h)
+        an = flat[which][pos]
+        assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (names[which], pos, fd, an)
+
+
+def _autograd_ref(q, k, v, dO, scale, mask):
+    def t(a):
+        return torch.tensor(np.transpose(a, (0, 2, 1, 3)), dtype=torch.float64,
+                            requires_grad=True)
+    qt, kt, vt = t(q), t(k), t(v)
+    am = None if mask is None else torch.from_numpy(mask)
+    o = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=am, scale=scale)
+    (o * torch.from_numpy(np.transpose(dO, (0, 2, 1, 3)))).sum().backward()
+    return [np.transpose(a.grad.numpy(), (0, 2, 1, 3)) for a in (qt, kt, vt)]
+
+
+@pytest.mark.parametrize("r", [2, 7])
+def test_matches_torch_autograd(r):
+    p, x, dO, _ = _tiny(1)
+    scale = 1 / math.sqrt(p.head_dim)
+    qm, km = orc.block_pool(x["q"], p), orc.block_pool(x["k"], p)
+    idx, _ = orc.select_topr(qm, km, p, r)
+    toks = orc.noise_cube_tokens(p)
+    M = np.zeros((p.Nq, p.Nq), dtype=bool)
+    for i in range(p.nbq):
+        for j in idx[0, 0, i]:
+            M[np.ix_(toks[i], toks[int(j)])] = True
+    ref = _autograd_ref(x["q"], x["k"], x["v"], dO, scale, None if r >= p.nbq - 1 else M)
+    got = orc.attn_bwd(x["q"], x["k"], x["v"], dO, idx, p, scale)
+    for g, rf in zip(got, ref):
+        np.testing.assert_allclose(g, rf, atol=1e-12, rtol=0)
+
+
+def test_gradient_invariants_multihead():
+    p = orc.Problem(2, 2, 16, 4, 8, 8, 2, 4, 4)
+    rng = np.random.default_rng(31)
+    q, k, v, dO = (rng.standard_normal((2, p.Nq, 2, 16)) for _ in range(4))
+    qm, km = orc.block_pool(q, p), orc.block_pool(k, p)
+    idx, _ = orc.select_topr(qm, km, p, 3)
+    dQ, dK, dV = orc.attn_bwd(q, k, v, dO, idx, p, 0.3)
+    # dV: every query's dO is spread by a probability row -> totals match
+    np.testing.assert_allclose(dV.sum(axis=1), dO.sum(axis=1), atol=1e-12)
+    # dK: each dS row sums to zero
+    np.testing.assert_allclose(dK.sum(axis=1), 0.0, atol=1e-12)
+    # scaling Q by a and K by 1/a leaves the output unchanged
+    lhs = np.einsum("bnhd,bnhd->bh", dQ, q)
+    rhs = np.einsum("bnhd,bnhd->bh", dK, k)
+    np.testing.assert_allclose(lhs, rhs, atol=1e-12)
+
+
+def test_selective_rows_and_key_cubes_match_full():
+    p, x, dO, w = _tiny(2)
+    qm, km = orc.block_pool(x["q"], p), orc.block_pool(x["k"], p)
+    idx, _ = orc.select_topr(qm, km, p, w.r)
+    full = orc.attn_bwd(x["q"], x["k"], x["v"], dO, idx, p, 0.125)
+    rows = [(0, 0, 1), (0, 0, 6)]
+    cols = [(0, 0, 0), (0, 0, 4)]
+    dq, dk, dv = orc.attn_bwd(x["q"], x["k"], x["v"], dO, idx, p, 0.125, rows=rows,
+                              key_cubes=cols)
+    toks = orc.noise_cube_tokens(p)
+    for key in rows:
+        np.testing.assert_allclose(dq[key], full[0][0, toks[key[2]], 0], atol=1e-14)
+    for key in cols:
+        np.testing.assert_allclose(dk[key], full[1][0, toks[key[2]], 0], atol=1e-14)
+        np.testing.assert_allclose(dv[key], full[2][0, toks[key[2]], 0], atol=1e-14)
+
+
+def test_transpose_selection_and_delta():
+    p, x, dO, w = _tiny(3)
+    qm, km = orc.block_pool(x["q"], p), orc.block_pool(x["k"], p)
+    idx, mask = orc.select_topr(qm, km, p, w.r)
+    off, lists = orc.transpose_selection(idx[0, 0], p.nbk)
+    for j in range(p.nbk):
+        expect = list(np.nonzero(mask[0, 0, :, j])[0])
+        assert list(lists[off[j]:off[j + 1]]) == expect
+    O, _ = orc.sparse_attn_fwd(x["q"], x["k"], x["v"], None, None, idx, p, 0.125)
+    d = orc.delta_rows(O, dO)
+    np.testing.assert_allclose(d[0, 0, 17], float(np.dot(O[0, 17, 0], dO[0, 17, 0])), atol=1e-14)
