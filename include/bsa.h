@@ -66,7 +66,7 @@ typedef enum { BSA_F32 = 0, BSA_BF16 = 1 } bsa_dtype_t;
  * condition cache and plain (non-causal) block-sparse attention.
  * Requirements: all sizes > 0 except cond_T >= 0; head_dim in {64, 128}; T - cond_T, H and W
  * divisible by cube_t, cube_h, cube_w; cond_T divisible by cube_t and cond_T < T;
- * cube size c = cube_t*cube_h*cube_w <= 256. */
+ * cube size c = cube_t*cube_h*cube_w <= 256; per (b, h) at most 40000 noise cubes. */
 typedef struct {
   int32_t batch, heads, head_dim; /* B, Hh, D                                  */
   int32_t T, H, W;                /* latent grid, condition frames included    */
@@ -150,14 +150,19 @@ const char* bsa_status_string(bsa_status_t s);
 /* Text of the last argument error raised on this thread (static per thread, never NULL). */
 const char* bsa_last_error(void);
 
-/* Stage timing for profiling.  When events != NULL, every entry point records events[k] (HIP
- * events created by the caller) on its stream at the boundaries of its internal kernels: slot 0
- * before the first launch and slot s after internal stage s, for s < n.  Stage slots are listed
- * by bsa_stage_name(); pass NULL to disable.  The setting is per host thread. */
+/* Stage timing for profiling.  When events != NULL, every entry point records HIP events (created
+ * by the caller) on its stream at the boundaries of its internal kernels: events[0] before the
+ * first launch and events[s + 1] after internal stage s, for slots < n.  Stage s spans
+ * events[s] -> events[s + 1]; bsa_stage_count() and bsa_stage_name() describe the stages of the
+ * last entry point called on this thread.  Pass NULL to disable.  The setting is per host thread. */
 void bsa_set_stage_events(hipEvent_t* events, int32_t n);
+int32_t bsa_stage_count(void);
+const char* bsa_stage_name(int32_t s); /* "" when s is out of range */
 
-/* Name of internal stage s of the last entry point called on this thread ("" when none). */
-const char* bsa_stage_name(int32_t s);
+/* Kernel path selection (testing and diagnostics), per host thread: 0 = automatic (bf16 MFMA
+ * kernels for 64-token cubes, portable fp32-arithmetic kernels otherwise), 1 = always the
+ * portable kernels.  Returns BSA_ERR_INVALID_ARG for other values. */
+bsa_status_t bsa_set_kernel_path(int32_t path);
 
 #ifdef __cplusplus
 }

@@ -1,0 +1,113 @@
+"""The C ABI library loads, exports every symbol include/bsa.h declares, and rejects bad
+arguments on the host before any HIP call (CPU only: no kernel is launched here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from video_dit_block_cube_amd import bsa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bsa.h")
+
+OK, INVALID, SHAPE, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3, 4
+FAKE = ctypes.c_void_p(0x10000)  # never dereferenced: every case below fails validation first
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(bsa_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(bsa.LIB_PATH):
+        pytest.fail("libbsa.so is not built (run __graft_entry__.build())")
+    return bsa.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(L, n), f"{n} declared in bsa.h but not exported"
+
+
+def _p(**kw):
+    base = dict(batch=1, heads=2, head_dim=128, T=8, H=8, W=8, cube_t=4, cube_h=4, cube_w=4,
+                cond_T=0)
+    base.update(kw)
+    return bsa.Problem(**base).c_struct()
+
+
+def test_num_selected_and_workspace(L):
+    assert L.bsa_num_selected(ctypes.byref(_p()), 2) == 3
+    assert L.bsa_num_selected(ctypes.byref(_p()), 100) == 8          # clamped to nbq
+    assert L.bsa_num_selected(ctypes.byref(_p(T=8, cond_T=4)), 0) == 4 + 1
+    assert L.bsa_num_selected(ctypes.byref(_p()), -1) == -1
+    assert L.bsa_num_selected(ctypes.byref(_p(T=7)), 1) == -1
+    big = bsa.Problem(1, 32, 128, 24, 48, 80, 4, 4, 4)
+    assert bsa.bsa_num_selected(big, 144) == 145
+    import torch
+    fwd = bsa.bsa_workspace_bytes(big, torch.bfloat16, 145, False)
+    assert fwd == 2 * 32 * 1440 * 64 * 128 * 2                      # K rows + V^T, bf16
+    assert bsa.bsa_workspace_bytes(big, torch.float32, 145, False) == 0
+    assert bsa.bsa_workspace_bytes(big, torch.bfloat16, 145, True) > fwd
+    with pytest.raises(bsa.BsaError):
+        bsa.bsa_workspace_bytes(big, torch.bfloat16, 1441, False)
+
+
+@pytest.mark.parametrize("kw, status", [
+    (dict(T=7), SHAPE), (dict(W=10), SHAPE), (dict(cond_T=2), SHAPE), (dict(cond_T=8), SHAPE),
+    (dict(head_dim=96), UNSUPPORTED), (dict(cube_t=8, cube_h=8, cube_w=8, T=8, H=8, W=8),
+                                       UNSUPPORTED),
+    (dict(heads=0), INVALID), (dict(cond_T=-4), INVALID),
+])
+def test_problem_rules(L, kw, status):
+    st = L.bsa_block_pool(ctypes.byref(_p(**kw)), 1, FAKE, FAKE, None)
+    assert st == status, (kw, st, L.bsa_last_error())
+
+
+def test_argument_errors(L):
+    p = ctypes.byref(_p())
+    assert L.bsa_block_pool(None, 1, FAKE, FAKE, None) == INVALID
+    assert L.bsa_block_pool(p, 7, FAKE, FAKE, None) == INVALID
+    assert L.bsa_block_pool(p, 1, None, FAKE, None) == INVALID
+    assert L.bsa_select_topr(p, FAKE, FAKE, -1, FAKE, None, None) == INVALID
+    assert L.bsa_select_topr(p, FAKE, None, 2, FAKE, None, None) == INVALID
+    fwd = L.bsa_sparse_attn_fwd
+    # k_sel inconsistent with any r
+    assert fwd(p, 1, FAKE, FAKE, FAKE, None, None, FAKE, 0, ctypes.c_float(0.1), FAKE, FAKE,
+               FAKE, 1 << 40, None) == INVALID
+    assert fwd(p, 1, FAKE, FAKE, FAKE, None, None, FAKE, 9, ctypes.c_float(0.1), FAKE, FAKE,
+               FAKE, 1 << 40, None) == INVALID
+    # cache given without condition frames, and missing with them
+    assert fwd(p, 1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 3, ctypes.c_float(0.1), FAKE, FAKE,
+               FAKE, 1 << 40, None) == INVALID
+    pc = ctypes.byref(_p(T=8, cond_T=4))
+    assert fwd(pc, 1, FAKE, FAKE, FAKE, None, None, FAKE, 5, ctypes.c_float(0.1), FAKE, FAKE,
+               FAKE, 1 << 40, None) == INVALID
+    # workspace too small for the bf16 MFMA path
+    assert fwd(p, 1, FAKE, FAKE, FAKE, None, None, FAKE, 3, ctypes.c_float(0.1), FAKE, FAKE,
+               FAKE, 16, None) == WORKSPACE
+    assert fwd(p, 1, FAKE, FAKE, FAKE, None, None, FAKE, 3, ctypes.c_float(float("nan")), FAKE,
+               FAKE, FAKE, 1 << 40, None) == INVALID
+    bwd = L.bsa_sparse_attn_bwd
+    assert bwd(pc, 1, *[FAKE] * 7, 5, ctypes.c_float(0.1), FAKE, FAKE, FAKE, FAKE, 1 << 40,
+               None) == UNSUPPORTED
+    assert bwd(p, 1, *[FAKE] * 7, 3, ctypes.c_float(0.1), FAKE, FAKE, FAKE, FAKE, 8,
+               None) == WORKSPACE
+    assert bwd(p, 1, *[FAKE] * 6, None, 3, ctypes.c_float(0.1), FAKE, FAKE, FAKE, FAKE, 1 << 40,
+               None) == INVALID
+    assert L.bsa_last_error()  # a message is kept for the last failure
+
+
+def test_status_strings_and_path_switch(L):
+    for code, name in bsa.STATUS.items():
+        assert bsa.bsa_status_string(code) == name
+    assert L.bsa_set_kernel_path(2) == INVALID
+    assert L.bsa_set_kernel_path(1) == OK
+    assert L.bsa_set_kernel_path(0) == OK
+    assert L.bsa_stage_name(-1) == b""

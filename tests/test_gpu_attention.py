@@ -1,0 +1,199 @@
+"""GPU parity of the sparse attention forward and backward against the fp64 oracle (through the
+C ABI).  Both sides use the same selection (idx computed once and shared), so these tests check
+the attention arithmetic; selection parity is covered in test_gpu_pool_select.
+
+Tolerances: fp32 max-abs 1e-4, bf16 max-abs 2e-2, plus relative-L2 bounds (1e-5 / 1e-2)."""
+import numpy as np
+import pytest
+
+import oracle as orc
+from tests._util import (assert_close, cached_inputs, print_case, sample_rows, scale_of, to_dev)
+from video_dit_block_cube_amd import bsa, synth
+
+pytestmark = pytest.mark.gpu
+
+PORTABLE, AUTO = 1, 0
+
+
+@pytest.fixture(autouse=True)
+def _auto_path():
+    yield
+    bsa.bsa_set_kernel_path(AUTO)
+
+
+def _setup(w, x, r, idx=None):
+    p = bsa.Problem(**w.shape_dict)
+    op = orc.Problem(**w.shape_dict)
+    if idx is None:
+        qm, km = orc.block_pool(x["q"], op), orc.block_pool(x["k"], op)
+        idx, _ = orc.select_topr(qm, km, op, r)
+    t = {k: to_dev(v, w.dtype) for k, v in x.items()}
+    return p, op, idx, t
+
+
+def _fwd(p, t, idx, ks, scale):
+    return bsa.bsa_sparse_attn_fwd(p, t["q"], t["k"], t["v"], _idx_dev(idx), ks, scale,
+                                   t.get("k_cache"), t.get("v_cache"))
+
+
+def _idx_dev(idx):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(idx, dtype=np.int32)).to("cuda:0")
+
+
+SMALL = [
+    # (workload, overrides, r, path)
+    (1, (), 2, AUTO),                                                   # tiny fp32
+    (1, (), 7, AUTO),                                                   # tiny fp32, dense
+    (2, (("batch", 2), ("heads", 3), ("T", 8), ("H", 8), ("W", 16)), 3, AUTO),    # bf16 MFMA
+    (2, (("batch", 2), ("heads", 3), ("T", 8), ("H", 8), ("W", 16)), 3, PORTABLE),
+    (2, (("heads", 2), ("head_dim", 64), ("T", 8), ("H", 8), ("W", 16)), 4, AUTO),  # D = 64
+    (2, (("heads", 2), ("T", 4), ("H", 8), ("W", 12)), 2, AUTO),        # nbq = 6 (not /8)
+    (2, (("heads", 2), ("T", 8), ("H", 8), ("W", 16)), 15, AUTO),       # dense bf16
+    (2, (("heads", 1), ("T", 4), ("H", 4), ("W", 4)), 3, AUTO),         # one cube, k_sel = 1
+    (1, (("heads", 3), ("T", 6), ("H", 12), ("W", 10), ("cube_t", 2), ("cube_h", 3),
+         ("cube_w", 5)), 3, AUTO),                                      # 30-token cubes fp32
+    (2, (("heads", 2), ("head_dim", 128), ("T", 6), ("H", 12), ("W", 10), ("cube_t", 2),
+         ("cube_h", 3), ("cube_w", 5)), 3, AUTO),                       # 30-token cubes bf16
+    (1, (("heads", 2), ("T", 4), ("H", 8), ("W", 8), ("cube_t", 4), ("cube_h", 8),
+         ("cube_w", 4)), 1, AUTO),                                      # 128-token cubes fp32
+    (1, (("heads", 2), ("T", 2), ("H", 4), ("W", 4), ("cube_t", 1), ("cube_h", 1),
+         ("cube_w", 1)), 5, AUTO),                                      # 1-token cubes
+]
+
+
+@pytest.mark.parametrize("number, over, r, path", SMALL)
+def test_fwd_small(number, over, r, path):
+    w, x = cached_inputs(number, over)
+    print_case(f"fwd {w.name} {dict(over)} r={r} path={path}")
+    bsa.bsa_set_kernel_path(path)
+    p, op, idx, t = _setup(w, x, r)
+    ks = orc.num_selected(op, r)
+    scale = scale_of(op)
+    o, lse = _fwd(p, t, idx, ks, scale)
+    O, LSE = orc.sparse_attn_fwd(x["q"], x["k"], x["v"], None, None, idx, op, scale)
+    assert_close(o.float().cpu().numpy(), O, w.dtype, "O")
+    assert_close(lse.cpu().numpy(), LSE, w.dtype, "LSE", max_abs=1e-4 if w.dtype == "f32" else 2e-3,
+                 rel=1e-5)
+
+
+@pytest.mark.parametrize("path", [AUTO, PORTABLE])
+def test_fwd_continuation_small(path):
+    w = synth.workload(4, batch=2, heads=2, T=12, H=8, W=16, cond_T=4)
+    x = synth.make_inputs(w)
+    print_case(f"fwd continuation small path={path}")
+    bsa.bsa_set_kernel_path(path)
+    p, op, idx, t = _setup(w, x, 3)
+    ks = orc.num_selected(op, 3)
+    scale = scale_of(op)
+    o, lse = _fwd(p, t, idx, ks, scale)
+    O, LSE = orc.sparse_attn_fwd(x["q"], x["k"], x["v"], x["k_cache"], x["v_cache"], idx, op,
+                                 scale)
+    assert_close(o.float().cpu().numpy(), O, "bf16", "O")
+    assert_close(lse.cpu().numpy(), LSE, "bf16", "LSE", max_abs=2e-3, rel=1e-5)
+
+
+def _gpu_selection(w, t, p):
+    qm = bsa.bsa_block_pool(p, t["q"])
+    km = bsa.bsa_block_pool(p, t["k"])
+    idx, _ = bsa.bsa_select_topr(p, qm, km, w.r, with_mask=False)
+    return idx
+
+
+@pytest.mark.parametrize("number", [2, 3, 4])
+def test_fwd_full_size_sampled(number):
+    w, x = cached_inputs(number)
+    print_case(f"fwd full {w.name}")
+    p = bsa.Problem(**w.shape_dict)
+    op = orc.Problem(**w.shape_dict)
+    t = {k: to_dev(v, w.dtype) for k, v in x.items()}
+    idx_d = _gpu_selection(w, t, p)
+    ks = orc.num_selected(op, w.r)
+    scale = scale_of(op)
+    o, lse = bsa.bsa_sparse_attn_fwd(p, t["q"], t["k"], t["v"], idx_d, ks, scale,
+                                     t.get("k_cache"), t.get("v_cache"))
+    idx = idx_d.cpu().numpy()
+    o = o.float().cpu().numpy()
+    lse = lse.cpu().numpy()
+    rows = sample_rows(op, [0, 15, 31], 4 if number == 4 else 6, seed=number)
+    res = orc.attn_fwd_rows(x["q"], x["k"], x["v"], x.get("k_cache"), x.get("v_cache"), idx, op,
+                            scale, rows)
+    toks = orc.noise_cube_tokens(op)
+    got_o = np.stack([o[b, toks[i], h] for (b, h, i) in rows])
+    ref_o = np.stack([res[k][0] for k in rows])
+    got_l = np.stack([lse[b, h, toks[i]] for (b, h, i) in rows])
+    ref_l = np.stack([res[k][1] for k in rows])
+    assert_close(got_o, ref_o, "bf16", "O")
+    assert_close(got_l, ref_l, "bf16", "LSE", max_abs=2e-3, rel=1e-5)
+    # properties at full size: finite everywhere, every output row in the hull of V
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    assert np.abs(o).max() <= np.abs(x["v"]).max() + 1e-2
+
+
+BWD_SMALL = [
+    (1, (), 2, AUTO),                                                   # tiny fp32 (portable)
+    (5, (("batch", 2), ("heads", 2), ("T", 8), ("H", 8), ("W", 16)), 3, AUTO),   # bf16 MFMA
+    (5, (("batch", 2), ("heads", 2), ("T", 8), ("H", 8), ("W", 16)), 3, PORTABLE),
+    (5, (("heads", 2), ("head_dim", 64), ("T", 8), ("H", 8), ("W", 16)), 4, AUTO),   # D = 64
+    (5, (("heads", 2), ("T", 4), ("H", 8), ("W", 12)), 2, AUTO),        # nbq = 6
+    (5, (("heads", 1), ("T", 8), ("H", 8), ("W", 16)), 15, AUTO),       # dense
+    (5, (("heads", 1), ("T", 4), ("H", 4), ("W", 4)), 0, AUTO),         # one cube
+    (1, (("heads", 2), ("T", 6), ("H", 12), ("W", 10), ("cube_t", 2), ("cube_h", 3),
+         ("cube_w", 5)), 3, AUTO),                                      # 30-token cubes fp32
+]
+
+
+def _dO(w, x):
+    if "dO" in x:
+        return x["dO"]
+    rng = np.random.default_rng(4242)
+    return rng.standard_normal(x["q"].shape).astype(np.float32)
+
+
+@pytest.mark.parametrize("number, over, r, path", BWD_SMALL)
+def test_bwd_small(number, over, r, path):
+    w, x = cached_inputs(number, over)
+    print_case(f"bwd {w.name} {dict(over)} r={r} path={path}")
+    bsa.bsa_set_kernel_path(path)
+    dO = _dO(w, x)
+    p, op, idx, t = _setup(w, x, r)
+    t["dO"] = to_dev(dO, w.dtype)
+    ks = orc.num_selected(op, r)
+    scale = scale_of(op)
+    o, lse = _fwd(p, t, idx, ks, scale)
+    dq, dk, dv = bsa.bsa_sparse_attn_bwd(p, t["q"], t["k"], t["v"], o, t["dO"], lse,
+                                         _idx_dev(idx), ks, scale)
+    ref = orc.attn_bwd(x["q"], x["k"], x["v"], dO, idx, op, scale)
+    for name, got, rf in zip(("dQ", "dK", "dV"), (dq, dk, dv), ref):
+        assert_close(got.cpu().numpy(), rf, w.dtype, name)
+
+
+def test_bwd_full_size_sampled():
+    w, x = cached_inputs(5)
+    print_case(f"bwd full {w.name}")
+    p = bsa.Problem(**w.shape_dict)
+    op = orc.Problem(**w.shape_dict)
+    t = {k: to_dev(v, w.dtype) for k, v in x.items()}
+    idx_d = _gpu_selection(w, t, p)
+    ks = orc.num_selected(op, w.r)
+    scale = scale_of(op)
+    o, lse = bsa.bsa_sparse_attn_fwd(p, t["q"], t["k"], t["v"], idx_d, ks, scale)
+    dq, dk, dv = bsa.bsa_sparse_attn_bwd(p, t["q"], t["k"], t["v"], o, t["dO"], lse, idx_d, ks,
+                                         scale)
+    idx = idx_d.cpu().numpy()
+    dq, dk, dv = (a.cpu().numpy() for a in (dq, dk, dv))
+    rows = sample_rows(op, [0, 31], 3, seed=11)
+    cols = sample_rows(op, [0, 31], 3, seed=12)
+    rq, rk, rv = orc.attn_bwd(x["q"], x["k"], x["v"], x["dO"], idx, op, scale, rows=rows,
+                              key_cubes=cols)
+    toks = orc.noise_cube_tokens(op)
+    assert_close(np.stack([dq[b, toks[i], h] for (b, h, i) in rows]),
+                 np.stack([rq[k] for k in rows]), "bf16", "dQ")
+    assert_close(np.stack([dk[b, toks[j], h] for (b, h, j) in cols]),
+                 np.stack([rk[k] for k in cols]), "bf16", "dK")
+    assert_close(np.stack([dv[b, toks[j], h] for (b, h, j) in cols]),
+                 np.stack([rv[k] for k in cols]), "bf16", "dV")
+    # properties at full size: sum_k dV = sum_q dO and sum_k dK = 0 per (b, h)
+    dO64 = x["dO"].astype(np.float64)
+    np.testing.assert_allclose(dv.sum(axis=1), dO64.sum(axis=1), atol=0.5, rtol=1e-2)
+    assert np.abs(dk.astype(np.float64).sum(axis=1)).max() < 0.5

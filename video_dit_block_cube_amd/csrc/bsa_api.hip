@@ -1,0 +1,353 @@
+// bsa_api.hip -- the C ABI of libbsa.so: argument checks, workspace carving, kernel dispatch.
+//
+// Entry points follow the statement of the method on the LongCat-Video pages: pool cubes and
+// pick the top-r key cubes per query cube ("LongCat-Video视频生成模型发布 迈出世界模型探索第一步",
+// youleyou, section "块稀疏注意力（BSA）"), attend only the selected cube pairs with an optional
+// cached condition segment ("LongCat-Video deep dive", ai-news-5min-kr, block-sparse attention
+// paragraph; "LongCat-Video 高效長視頻生成探索世界模型的第壹步", meituan.com talk, section 2.1),
+// and the backward (same talk, section 2.2).  Every check runs on the host before any HIP call.
+#include <cmath>
+#include <cstring>
+#include <exception>
+#include <string>
+
+#include "bsa.h"
+#include "bsa_launch.h"
+
+using namespace bsa;
+
+namespace {
+
+thread_local std::string t_err;
+thread_local hipEvent_t* t_events = nullptr;
+thread_local int t_nevents = 0;
+thread_local const char* t_stage_names[16];
+thread_local int t_nstages = 0;
+thread_local int t_path = 0;
+
+constexpr size_t kAlign = 256;
+constexpr int kMaxNoiseCubes = 40000;
+
+bsa_status_t fail(bsa_status_t st, const std::string& msg) {
+  t_err = msg;
+  return st;
+}
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Stage bookkeeping for the optional profiling events.
+struct Stages {
+  hipStream_t s;
+  explicit Stages(hipStream_t st) : s(st) {
+    t_nstages = 0;
+    if (t_events && t_nevents > 0) hipEventRecord(t_events[0], s);
+  }
+  void done(const char* name) {
+    if (t_nstages < 16) t_stage_names[t_nstages] = name;
+    ++t_nstages;
+    if (t_events && t_nstages < t_nevents) hipEventRecord(t_events[t_nstages], s);
+  }
+};
+
+bsa_status_t check_problem(const bsa_problem_t* p, Geom* g) {
+  if (!p) return fail(BSA_ERR_INVALID_ARG, "problem pointer is NULL");
+  if (p->batch <= 0 || p->heads <= 0 || p->head_dim <= 0 || p->T <= 0 || p->H <= 0 ||
+      p->W <= 0 || p->cube_t <= 0 || p->cube_h <= 0 || p->cube_w <= 0)
+    return fail(BSA_ERR_INVALID_ARG, "every size must be positive");
+  if (p->cond_T < 0) return fail(BSA_ERR_INVALID_ARG, "cond_T must be >= 0");
+  if (p->cond_T >= p->T) return fail(BSA_ERR_SHAPE, "cond_T must be < T");
+  if ((p->T - p->cond_T) % p->cube_t || p->H % p->cube_h || p->W % p->cube_w ||
+      p->cond_T % p->cube_t)
+    return fail(BSA_ERR_SHAPE, "grid (noise frames, H, W, cond_T) not divisible by the cube");
+  if (p->head_dim != 64 && p->head_dim != 128)
+    return fail(BSA_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+  const long long c = (long long)p->cube_t * p->cube_h * p->cube_w;
+  if (c > 256) return fail(BSA_ERR_UNSUPPORTED, "cube size must be <= 256 tokens");
+  const long long nbq = (long long)(p->T - p->cond_T) / p->cube_t * (p->H / p->cube_h) *
+                        (p->W / p->cube_w);
+  const long long nbc = (long long)p->cond_T / p->cube_t * (p->H / p->cube_h) * (p->W / p->cube_w);
+  if (nbq > kMaxNoiseCubes || nbc > kMaxNoiseCubes)
+    return fail(BSA_ERR_UNSUPPORTED, "at most 40000 cubes per segment");
+  const long long tokens = (long long)p->T * p->H * p->W;
+  if (tokens * p->heads * p->head_dim * p->batch > (1LL << 40))
+    return fail(BSA_ERR_UNSUPPORTED, "problem too large");
+  *g = make_geom(p->batch, p->heads, p->head_dim, p->T, p->H, p->W, p->cube_t, p->cube_h,
+                 p->cube_w, p->cond_T);
+  return BSA_OK;
+}
+
+bool use_mfma(const Geom& g, bsa_dtype_t dt) { return t_path == 0 && dt == BSA_BF16 && g.c == 64; }
+
+bsa_status_t check_dtype(bsa_dtype_t dt) {
+  if (dt != BSA_F32 && dt != BSA_BF16) return fail(BSA_ERR_INVALID_ARG, "unknown dtype");
+  return BSA_OK;
+}
+
+bsa_status_t check_ksel(const Geom& g, int32_t k_sel) {
+  if (k_sel < g.nbc + 1 || k_sel > g.nbk)
+    return fail(BSA_ERR_INVALID_ARG, "k_sel is not nbc + 1 + min(r, nbq - 1) for any r >= 0");
+  // CSR positions and per-(b, h) index arithmetic stay in int32
+  if ((long long)g.B * g.Hh * g.nbq * k_sel >= (1LL << 31))
+    return fail(BSA_ERR_UNSUPPORTED, "selection too large for int32 positions");
+  return BSA_OK;
+}
+
+bsa_status_t hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return BSA_OK;
+  return fail(BSA_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+// Workspace layout of the backward (and of the forward for the MFMA path).
+struct BwdWs {
+  size_t delta, lse, bits, off, list, g_qr, g_qt, g_dr, g_dt, g_kr, g_kt, g_vr, total;
+};
+
+BwdWs bwd_layout(const Geom& g, bool mfma, int k_sel) {
+  BwdWs w{};
+  size_t at = 0;
+  auto take = [&](size_t bytes) {
+    const size_t here = at;
+    at += align_up(bytes);
+    return here;
+  };
+  const size_t per_cube = (size_t)g.B * g.Hh * g.nbq * g.c * sizeof(float);
+  w.delta = take(per_cube);
+  w.lse = take(per_cube);
+  w.bits = take(csr_bits_words(g) * sizeof(uint32_t));
+  w.off = take((size_t)g.B * g.Hh * (g.nbk + 1) * sizeof(int32_t));
+  w.list = take((size_t)g.B * g.Hh * g.nbq * (size_t)k_sel * sizeof(int32_t));
+  if (mfma) {
+    const size_t gb = gather_bytes(g, true);
+    w.g_qr = take(gb);
+    w.g_qt = take(gb);
+    w.g_dr = take(gb);
+    w.g_dt = take(gb);
+    w.g_kr = take(gb);
+    w.g_kt = take(gb);
+    w.g_vr = take(gb);
+  }
+  w.total = at;
+  return w;
+}
+
+size_t fwd_ws(const Geom& g, bool mfma) {
+  return mfma ? 2 * align_up(gather_bytes(g, true)) : 0;
+}
+
+template <typename F>
+bsa_status_t guarded(F&& f) {
+  try {
+    return f();
+  } catch (const std::exception& e) {
+    return fail(BSA_ERR_INTERNAL, std::string("internal error: ") + e.what());
+  } catch (...) {
+    return fail(BSA_ERR_INTERNAL, "internal error");
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+bsa_status_t bsa_block_pool(const bsa_problem_t* p, bsa_dtype_t dtype, const void* x,
+                            float* x_mean, hipStream_t stream) {
+  return guarded([&]() -> bsa_status_t {
+    Geom g;
+    bsa_status_t st = check_problem(p, &g);
+    if (st != BSA_OK) return st;
+    if ((st = check_dtype(dtype)) != BSA_OK) return st;
+    if (!x || !x_mean) return fail(BSA_ERR_INVALID_ARG, "x and x_mean must be non-NULL");
+    Stages stages(stream);
+    st = hip_status(launch_pool(g, dtype == BSA_BF16, x, x_mean, stream), "pool launch");
+    stages.done("pool");
+    return st;
+  });
+}
+
+bsa_status_t bsa_select_topr(const bsa_problem_t* p, const float* q_mean, const float* k_mean,
+                             int32_t r, int32_t* idx, uint8_t* mask, hipStream_t stream) {
+  return guarded([&]() -> bsa_status_t {
+    Geom g;
+    bsa_status_t st = check_problem(p, &g);
+    if (st != BSA_OK) return st;
+    if (r < 0) return fail(BSA_ERR_INVALID_ARG, "r must be >= 0");
+    if (!q_mean || !k_mean || !idx)
+      return fail(BSA_ERR_INVALID_ARG, "q_mean, k_mean and idx must be non-NULL");
+    const int r_eff = r < g.nbq - 1 ? r : g.nbq - 1;
+    const int k_sel = g.nbc + 1 + r_eff;
+    if ((st = check_ksel(g, k_sel)) != BSA_OK) return st;
+    Stages stages(stream);
+    st = hip_status(launch_select(g, q_mean, k_mean, r_eff, k_sel, idx, mask, stream),
+                    "select launch");
+    stages.done("select");
+    return st;
+  });
+}
+
+bsa_status_t bsa_sparse_attn_fwd(const bsa_problem_t* p, bsa_dtype_t dtype, const void* q,
+                                 const void* k, const void* v, const void* k_cache,
+                                 const void* v_cache, const int32_t* idx, int32_t k_sel,
+                                 float softmax_scale, void* o, float* lse, void* ws,
+                                 size_t ws_bytes, hipStream_t stream) {
+  return guarded([&]() -> bsa_status_t {
+    Geom g;
+    bsa_status_t st = check_problem(p, &g);
+    if (st != BSA_OK) return st;
+    if ((st = check_dtype(dtype)) != BSA_OK) return st;
+    if ((st = check_ksel(g, k_sel)) != BSA_OK) return st;
+    if (!q || !k || !v || !idx || !o || !lse)
+      return fail(BSA_ERR_INVALID_ARG, "q, k, v, idx, o and lse must be non-NULL");
+    if (g.condT > 0 && (!k_cache || !v_cache))
+      return fail(BSA_ERR_INVALID_ARG, "cond_T > 0 needs k_cache and v_cache");
+    if (g.condT == 0 && (k_cache || v_cache))
+      return fail(BSA_ERR_INVALID_ARG, "k_cache / v_cache given but cond_T == 0");
+    if (!std::isfinite(softmax_scale)) return fail(BSA_ERR_INVALID_ARG, "softmax_scale not finite");
+    const bool mfma = use_mfma(g, dtype);
+    const size_t need = fwd_ws(g, mfma);
+    if (need > 0 && (!ws || ws_bytes < need))
+      return fail(BSA_ERR_WORKSPACE, "workspace smaller than bsa_workspace_bytes()");
+    Stages stages(stream);
+    if (mfma) {
+      bf16_t* krow = static_cast<bf16_t*>(ws);
+      bf16_t* vtr = reinterpret_cast<bf16_t*>(static_cast<char*>(ws) +
+                                              align_up(gather_bytes(g, true)));
+      st = hip_status(launch_gather(g, k, k_cache, GATHER_ROW, krow, nullptr, stream),
+                      "gather K");
+      if (st != BSA_OK) return st;
+      st = hip_status(launch_gather(g, v, v_cache, GATHER_TRANS, nullptr, vtr, stream),
+                      "gather V");
+      if (st != BSA_OK) return st;
+      stages.done("gather_kv");
+      st = hip_status(launch_fwd_mfma(g, q, krow, vtr, idx, k_sel, softmax_scale, o, lse, stream),
+                      "attention forward launch");
+      stages.done("attn_fwd_mfma");
+    } else {
+      st = hip_status(launch_fwd_simt(g, dtype == BSA_BF16, q, k, v, k_cache, v_cache, idx,
+                                      k_sel, softmax_scale, o, lse, stream),
+                      "attention forward launch");
+      stages.done("attn_fwd_simt");
+    }
+    return st;
+  });
+}
+
+bsa_status_t bsa_sparse_attn_bwd(const bsa_problem_t* p, bsa_dtype_t dtype, const void* q,
+                                 const void* k, const void* v, const void* o, const void* d_o,
+                                 const float* lse, const int32_t* idx, int32_t k_sel,
+                                 float softmax_scale, float* dq, float* dk, float* dv, void* ws,
+                                 size_t ws_bytes, hipStream_t stream) {
+  return guarded([&]() -> bsa_status_t {
+    Geom g;
+    bsa_status_t st = check_problem(p, &g);
+    if (st != BSA_OK) return st;
+    if ((st = check_dtype(dtype)) != BSA_OK) return st;
+    if (g.condT != 0)
+      return fail(BSA_ERR_UNSUPPORTED, "backward needs cond_T == 0 (no condition-cache grads)");
+    if ((st = check_ksel(g, k_sel)) != BSA_OK) return st;
+    if (!q || !k || !v || !o || !d_o || !lse || !idx || !dq || !dk || !dv)
+      return fail(BSA_ERR_INVALID_ARG, "every tensor pointer must be non-NULL");
+    if (!std::isfinite(softmax_scale)) return fail(BSA_ERR_INVALID_ARG, "softmax_scale not finite");
+    const bool mfma = use_mfma(g, dtype);
+    const BwdWs w = bwd_layout(g, mfma, k_sel);
+    if (!ws || ws_bytes < w.total)
+      return fail(BSA_ERR_WORKSPACE, "workspace smaller than bsa_workspace_bytes()");
+    char* base = static_cast<char*>(ws);
+    float* delta_c = reinterpret_cast<float*>(base + w.delta);
+    float* lse_c = reinterpret_cast<float*>(base + w.lse);
+    uint32_t* bits = reinterpret_cast<uint32_t*>(base + w.bits);
+    int32_t* off = reinterpret_cast<int32_t*>(base + w.off);
+    int32_t* list = reinterpret_cast<int32_t*>(base + w.list);
+    const bool bf16 = dtype == BSA_BF16;
+    Stages stages(stream);
+    st = hip_status(launch_delta(g, bf16, o, d_o, lse, delta_c, lse_c, stream), "delta launch");
+    if (st != BSA_OK) return st;
+    st = hip_status(launch_csr(g, idx, k_sel, bits, off, list, stream), "csr launch");
+    if (st != BSA_OK) return st;
+    stages.done("bwd_prep");
+    if (mfma) {
+      auto at = [&](size_t o2) { return reinterpret_cast<bf16_t*>(base + o2); };
+      st = hip_status(launch_gather(g, q, nullptr, GATHER_ROW | GATHER_TRANS, at(w.g_qr),
+                                    at(w.g_qt), stream), "gather Q");
+      if (st != BSA_OK) return st;
+      st = hip_status(launch_gather(g, d_o, nullptr, GATHER_ROW | GATHER_TRANS, at(w.g_dr),
+                                    at(w.g_dt), stream), "gather dO");
+      if (st != BSA_OK) return st;
+      st = hip_status(launch_gather(g, k, nullptr, GATHER_ROW | GATHER_TRANS, at(w.g_kr),
+                                    at(w.g_kt), stream), "gather K");
+      if (st != BSA_OK) return st;
+      st = hip_status(launch_gather(g, v, nullptr, GATHER_ROW, at(w.g_vr), nullptr, stream),
+                      "gather V");
+      if (st != BSA_OK) return st;
+      stages.done("gather_qkv_do");
+      st = hip_status(launch_bwd_dkdv_mfma(g, k, v, at(w.g_qr), at(w.g_qt), at(w.g_dr),
+                                           at(w.g_dt), lse_c, delta_c, off, list,
+                                           softmax_scale, dk, dv, stream), "dK/dV launch");
+      if (st != BSA_OK) return st;
+      stages.done("bwd_dkdv_mfma");
+      st = hip_status(launch_bwd_dq_mfma(g, q, d_o, at(w.g_kr), at(w.g_kt), at(w.g_vr), lse_c,
+                                         delta_c, idx, k_sel, softmax_scale, dq, stream),
+                      "dQ launch");
+      stages.done("bwd_dq_mfma");
+    } else {
+      st = hip_status(launch_bwd_dkdv_simt(g, bf16, q, k, v, d_o, lse_c, delta_c, off, list,
+                                           softmax_scale, dk, dv, stream), "dK/dV launch");
+      if (st != BSA_OK) return st;
+      stages.done("bwd_dkdv_simt");
+      st = hip_status(launch_bwd_dq_simt(g, bf16, q, k, v, d_o, lse_c, delta_c, idx, k_sel,
+                                         softmax_scale, dq, stream), "dQ launch");
+      stages.done("bwd_dq_simt");
+    }
+    return st;
+  });
+}
+
+int32_t bsa_num_selected(const bsa_problem_t* p, int32_t r) {
+  Geom g;
+  if (r < 0 || check_problem(p, &g) != BSA_OK) return -1;
+  return g.nbc + 1 + (r < g.nbq - 1 ? r : g.nbq - 1);
+}
+
+size_t bsa_workspace_bytes(const bsa_problem_t* p, bsa_dtype_t dtype, int32_t k_sel,
+                           int32_t bwd) {
+  Geom g;
+  if (check_problem(p, &g) != BSA_OK || check_dtype(dtype) != BSA_OK ||
+      check_ksel(g, k_sel) != BSA_OK)
+    return (size_t)-1;
+  const bool mfma = use_mfma(g, dtype);
+  return bwd ? bwd_layout(g, mfma, k_sel).total : fwd_ws(g, mfma);
+}
+
+const char* bsa_status_string(bsa_status_t s) {
+  switch (s) {
+    case BSA_OK: return "BSA_OK";
+    case BSA_ERR_INVALID_ARG: return "BSA_ERR_INVALID_ARG";
+    case BSA_ERR_SHAPE: return "BSA_ERR_SHAPE";
+    case BSA_ERR_UNSUPPORTED: return "BSA_ERR_UNSUPPORTED";
+    case BSA_ERR_WORKSPACE: return "BSA_ERR_WORKSPACE";
+    case BSA_ERR_HIP: return "BSA_ERR_HIP";
+    case BSA_ERR_INTERNAL: return "BSA_ERR_INTERNAL";
+  }
+  return "BSA_ERR_UNKNOWN";
+}
+
+const char* bsa_last_error(void) { return t_err.c_str(); }
+
+void bsa_set_stage_events(hipEvent_t* events, int32_t n) {
+  t_events = events;
+  t_nevents = events ? n : 0;
+}
+
+int32_t bsa_stage_count(void) { return t_nstages; }
+
+const char* bsa_stage_name(int32_t s) {
+  if (s < 0 || s >= t_nstages || s >= 16) return "";
+  return t_stage_names[s];
+}
+
+bsa_status_t bsa_set_kernel_path(int32_t path) {
+  if (path != 0 && path != 1) return fail(BSA_ERR_INVALID_ARG, "path must be 0 or 1");
+  t_path = path;
+  return BSA_OK;
+}
+
+}  // extern "C"

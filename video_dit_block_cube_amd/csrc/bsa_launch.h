@@ -1,0 +1,67 @@
+// bsa_launch.h -- host-side launchers of the BSA kernels (one translation unit per kernel family).
+// Every launcher enqueues asynchronously on `stream` and returns the launch status.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "bsa_common.h"
+
+namespace bsa {
+
+// k_pool.hip: per-cube mean of a [B, Nq, Hh, D] tensor -> [B, Hh, nbq, D] fp32.
+hipError_t launch_pool(const Geom& g, bool bf16, const void* x, float* out, hipStream_t s);
+
+// k_select.hip: block scores + forced set + top-r -> idx (ascending rows) and optional mask.
+hipError_t launch_select(const Geom& g, const float* qm, const float* km, int r_eff, int k_sel,
+                         int32_t* idx, uint8_t* mask, hipStream_t s);
+
+// k_attn_simt.hip: portable fp32-arithmetic attention kernels (any cube size, fp32 or bf16 I/O).
+hipError_t launch_fwd_simt(const Geom& g, bool bf16, const void* q, const void* k, const void* v,
+                           const void* kc, const void* vc, const int32_t* idx, int k_sel,
+                           float scale, void* o, float* lse, hipStream_t s);
+hipError_t launch_bwd_dq_simt(const Geom& g, bool bf16, const void* q, const void* k,
+                              const void* v, const void* d_o, const float* lse_c,
+                              const float* delta_c, const int32_t* idx, int k_sel, float scale,
+                              float* dq, hipStream_t s);
+hipError_t launch_bwd_dkdv_simt(const Geom& g, bool bf16, const void* q, const void* k,
+                                const void* v, const void* d_o, const float* lse_c,
+                                const float* delta_c, const int32_t* csr_off,
+                                const int32_t* csr_list, float scale, float* dk, float* dv,
+                                hipStream_t s);
+
+// k_bwd_prep.hip: Delta and LSE in cube order ([B, Hh, nbq, c]) and the CSR transpose of idx.
+hipError_t launch_delta(const Geom& g, bool bf16, const void* o, const void* d_o,
+                        const float* lse, float* delta_c, float* lse_c, hipStream_t s);
+size_t csr_bits_words(const Geom& g);
+hipError_t launch_csr(const Geom& g, const int32_t* idx, int k_sel, uint32_t* bits,
+                      int32_t* csr_off, int32_t* csr_list, hipStream_t s);
+
+// k_gather.hip: cube-major, MFMA-operand-ordered copies of a token tensor (c == 64, bf16).
+//   mode bit 1: "row" layout (lane = token, 8 consecutive d per lane);
+//   mode bit 2: "transposed" layout (lane = d, 8 tokens per lane, in S-accumulator key order).
+// Output cube ids cover the condition cubes (from x_cache) first, then the noise cubes.
+enum { GATHER_ROW = 1, GATHER_TRANS = 2 };
+size_t gather_bytes(const Geom& g, bool with_cache);
+hipError_t launch_gather(const Geom& g, const void* x, const void* x_cache, int mode,
+                         bf16_t* out_row, bf16_t* out_trans, hipStream_t s);
+
+// k_attn_mfma.hip: bf16 MFMA forward for c == 64, D in {64, 128}.
+hipError_t launch_fwd_mfma(const Geom& g, const void* q, const bf16_t* k_row,
+                           const bf16_t* v_trans, const int32_t* idx, int k_sel, float scale,
+                           void* o, float* lse, hipStream_t s);
+
+// k_bwd_mfma.hip: bf16 MFMA backward kernels for c == 64, D in {64, 128}.
+hipError_t launch_bwd_dq_mfma(const Geom& g, const void* q, const void* d_o,
+                              const bf16_t* k_row, const bf16_t* k_trans, const bf16_t* v_row,
+                              const float* lse_c, const float* delta_c, const int32_t* idx,
+                              int k_sel, float scale, float* dq, hipStream_t s);
+hipError_t launch_bwd_dkdv_mfma(const Geom& g, const void* k, const void* v,
+                                const bf16_t* q_row, const bf16_t* q_trans,
+                                const bf16_t* do_row, const bf16_t* do_trans,
+                                const float* lse_c, const float* delta_c,
+                                const int32_t* csr_off, const int32_t* csr_list, float scale,
+                                float* dk, float* dv, hipStream_t s);
+
+}  // namespace bsa
