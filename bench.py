@@ -1,0 +1,296 @@
+#!/usr/bin/env python3
+"""Benchmark of the block sparse attention hot path on one MI355X.
+
+One step = the whole path over one batch of the 720p-class workload (B=1, 32 heads, D=128,
+latent grid 24x48x80, 4x4x4 cubes, top-r=144 plus the own cube, QKNorm'd q/k, dO ~ N(0,1)):
+pool Q, pool K, select, sparse attention forward, backward (Delta + CSR transpose, gathers,
+dK/dV, dQ).  Inputs are resident in HBM before the timed region.
+
+value = effective TFLOP/s over the step, counting selected-block FLOPs only:
+forward 4*B*Hh*Nq*(k_sel*c)*D, backward 2.5x forward.  Per-kernel durations come from HIP events
+recorded by the library at its internal stage boundaries on the launch stream.
+
+Usage: python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--no-cpu] [--no-continuation]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "BSA fwd+bwd effective TFLOP/s & % bf16 MFMA peak; ms/call at 720p-class grid"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def fwd_flops(p, k_sel: int) -> float:
+    return 4.0 * p.batch * p.heads * p.Nq * (k_sel * p.c) * p.head_dim
+
+
+def kernel_flops(name: str, p, k_sel: int) -> float | None:
+    """Contraction FLOPs one launch of a kernel performs (2*m*n*k per GEMM over selected pairs)."""
+    one_gemm = 2.0 * p.batch * p.heads * p.Nq * (k_sel * p.c) * p.head_dim
+    return {"attn_fwd_mfma": 2 * one_gemm,      # S = QK^T, O = PV
+            "bwd_dkdv_mfma": 4 * one_gemm,      # S, dP, dV, dK
+            "bwd_dq_mfma": 3 * one_gemm}.get(name)   # S, dP, dQ
+
+
+def traffic_from_profile(stage: str):
+    """HBM bytes per launch measured by rocprofv3 counters (profiles/traffic_<stage>.txt), or None
+    when no measurement exists or the kernel source changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{stage}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    src = os.path.join(ROOT, kv.get("source", ""))
+    if not kv.get("source") or not os.path.exists(src):
+        return None
+    if hashlib.sha256(open(src, "rb").read()).hexdigest() != kv.get("source_sha256"):
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(x, op, idx, r, budget_s: float = 12.0):
+    """The fp64 oracle, as it is, on a bounded sample of the same workload: forward and backward
+    (every GEMM of the algorithm, scatter of key gradients skipped) for query cubes of head 0,
+    taken in order until the time budget is spent."""
+    import numpy as np
+    import oracle as orc
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    scale = 1.0 / math.sqrt(op.head_dim)
+    ks = idx.shape[-1]
+    per_cube = 4.0 * op.c * (ks * op.c) * op.head_dim * 3.5   # fwd + bwd (2.5x) per query cube
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        row = [(0, 0, n)]
+        orc.attn_fwd_rows(x["q"], x["k"], x["v"], None, None, idx, op, scale, row)
+        orc.attn_bwd(x["q"], x["k"], x["v"], x["dO"], idx, op, scale, rows=row, key_cubes=[])
+        n += 1
+        el = time.perf_counter() - t0
+        if (el >= budget_s and n >= 4) or n >= op.nbq:
+            break
+    return {"value": per_cube * n / el / 1e12, "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"fp64 oracle fwd+bwd of {n} query cubes (head 0) of the 720p-class workload "
+                      f"in {el:.1f} s; {len(os.sched_getaffinity(0))} host cores visible, "
+                      f"{threads} BLAS threads"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-continuation", action="store_true",
+                    help="skip the continuation-mode forward measurement")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="also run a plain device copy of this many MiB (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the block sparse "
+              "attention path here is single-GPU, see DESIGN.md for how it would shard.",
+              file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+    import oracle as orc
+    from video_dit_block_cube_amd import bsa, synth
+
+    dev = torch.device("cuda:0")
+    w = synth.workload(3, with_grad=True)
+    log(f"drawing inputs for {w.name} (seed {1000 + w.number})")
+    t0 = time.perf_counter()
+    x = synth.make_inputs(w)
+    log(f"inputs ready in {time.perf_counter() - t0:.1f} s")
+    p = bsa.Problem(**w.shape_dict)
+    op = orc.Problem(**w.shape_dict)
+    t = {k: torch.from_numpy(v).to(dev).to(torch.bfloat16) for k, v in x.items()}
+    ks = bsa.bsa_num_selected(p, w.r)
+    scale = 1.0 / math.sqrt(p.head_dim)
+
+    # buffers allocated once; the step writes into them
+    qm = torch.empty((p.batch, p.heads, p.nbq, p.head_dim), dtype=torch.float32, device=dev)
+    km = torch.empty_like(qm)
+    idx = torch.empty((p.batch, p.heads, p.nbq, ks), dtype=torch.int32, device=dev)
+    o = torch.empty_like(t["q"])
+    lse = torch.empty((p.batch, p.heads, p.Nq), dtype=torch.float32, device=dev)
+    dq = torch.empty(t["q"].shape, dtype=torch.float32, device=dev)
+    dk = torch.empty_like(dq)
+    dv = torch.empty_like(dq)
+    ws_f = torch.empty(bsa.bsa_workspace_bytes(p, torch.bfloat16, ks, False), dtype=torch.uint8,
+                       device=dev)
+    ws_b = torch.empty(bsa.bsa_workspace_bytes(p, torch.bfloat16, ks, True), dtype=torch.uint8,
+                       device=dev)
+
+    def step(ev=None):
+        calls = [
+            lambda: bsa.bsa_block_pool(p, t["q"], qm),
+            lambda: bsa.bsa_block_pool(p, t["k"], km),
+            lambda: bsa.bsa_select_topr(p, qm, km, w.r, with_mask=False, idx=idx),
+            lambda: bsa.bsa_sparse_attn_fwd(p, t["q"], t["k"], t["v"], idx, ks, scale, o=o,
+                                            lse=lse, workspace=ws_f),
+            lambda: bsa.bsa_sparse_attn_bwd(p, t["q"], t["k"], t["v"], o, t["dO"], lse, idx, ks,
+                                            scale, dq=dq, dk=dk, dv=dv, workspace=ws_b),
+        ]
+        for ci, c in enumerate(calls):
+            if ev is None:
+                c()
+            else:
+                with ev[ci]:
+                    c()
+
+    log(f"warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: HIP events per internal stage of every call, on the launch stream
+    events = [[bsa.StageEvents(8) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    start = time.perf_counter()
+    for s in range(args.steps):
+        step(events[s])
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - start) * 1e3 / args.steps
+    stage_ms: dict[str, list] = {}
+    step_ms = []
+    for s in range(args.steps):
+        tot = 0.0
+        for ci in range(5):
+            for name, ms in events[s][ci].elapsed_all():
+                stage_ms.setdefault(name, []).append(ms)
+                tot += ms
+        step_ms.append(tot)
+    ms_per_step = wall_ms
+    log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step wall, "
+        f"{np.mean(step_ms):.3f} ms/step summed over kernels")
+
+    f_fwd = fwd_flops(p, ks)
+    eff = f_fwd * 3.5
+    value = eff / (ms_per_step * 1e-3) / 1e12
+    avg = {k: float(np.mean(v)) for k, v in stage_ms.items()}
+    # pool runs twice per step; per-launch average is what the roofline wants
+    dominant = max((k for k in avg if kernel_flops(k, p, ks)), key=lambda k: avg[k])
+    dom_flops = kernel_flops(dominant, p, ks)
+    achieved = dom_flops / (avg[dominant] * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "kernel": dominant, "achieved": round(achieved, 2),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": traffic_from_profile(dominant),
+                "flops_per_launch": dom_flops, "avg_launch_ms": round(avg[dominant], 4)}
+    per_kernel = {}
+    for k, v in avg.items():
+        kf = kernel_flops(k, p, ks)
+        per_kernel[k] = {"avg_ms": round(v, 4),
+                         **({"tflops": round(kf / (v * 1e-3) / 1e12, 1),
+                             "frac_peak": round(kf / (v * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+                            if kf else {})}
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "720p-class BSA fwd+bwd: B=1, Hh=32, D=128, grid 24x48x80, "
+                               "cube 4x4x4, top-r=144 + own cube, QKNorm q/k, dO~N(0,1)",
+                   "k_sel": ks, "selected_fraction": round(ks / p.nbq, 4),
+                   "fwd_tflop": round(f_fwd / 1e12, 3),
+                   "bwd_tflop_effective": round(2.5 * f_fwd / 1e12, 3)},
+        "pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "fwd_ms": round(avg.get("gather_qkv", 0) + avg.get("attn_fwd_mfma", 0), 3),
+        "bwd_ms": round(sum(avg.get(k, 0) for k in ("bwd_prep", "gather_qkv_do",
+                                                      "bwd_dkdv_mfma", "bwd_dq_mfma")), 3),
+        "kernels": per_kernel,
+        "roofline": roofline,
+    }
+
+    if not args.no_continuation:
+        out["continuation_fwd"] = bench_continuation(bsa, synth, orc, torch, dev, args)
+
+    if args.calib_copy_mib:
+        n = args.calib_copy_mib * (1 << 20) // 4
+        a = torch.empty(n, dtype=torch.float32, device=dev).normal_()
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        log(f"calibration copy: {args.calib_copy_mib} MiB read + {args.calib_copy_mib} MiB written")
+
+    if not args.no_cpu:
+        log("CPU oracle baseline")
+        out["cpu_baseline"] = cpu_baseline(x, op, idx.cpu().numpy(), w.r)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def bench_continuation(bsa, synth, orc, torch, dev, args):
+    """Forward of the continuation workload (12 condition frames from the cache, top-r=72)."""
+    import numpy as np
+    w = synth.workload(4)
+    log(f"drawing inputs for {w.name}")
+    x = synth.make_inputs(w)
+    p = bsa.Problem(**w.shape_dict)
+    t = {k: torch.from_numpy(v).to(dev).to(torch.bfloat16) for k, v in x.items()}
+    del x
+    ks = bsa.bsa_num_selected(p, w.r)
+    scale = 1.0 / math.sqrt(p.head_dim)
+    qm = bsa.bsa_block_pool(p, t["q"])
+    km = bsa.bsa_block_pool(p, t["k"])
+    idx, _ = bsa.bsa_select_topr(p, qm, km, w.r, with_mask=False)
+    ws = torch.empty(bsa.bsa_workspace_bytes(p, torch.bfloat16, ks, False), dtype=torch.uint8,
+                     device=dev)
+    o = torch.empty_like(t["q"])
+    lse = torch.empty((p.batch, p.heads, p.Nq), dtype=torch.float32, device=dev)
+    for _ in range(2):
+        bsa.bsa_sparse_attn_fwd(p, t["q"], t["k"], t["v"], idx, ks, scale, t["k_cache"],
+                                t["v_cache"], o=o, lse=lse, workspace=ws)
+    torch.cuda.synchronize()
+    evs = [bsa.StageEvents(4) for _ in range(max(3, args.steps // 2))]
+    for ev in evs:
+        with ev:
+            bsa.bsa_sparse_attn_fwd(p, t["q"], t["k"], t["v"], idx, ks, scale, t["k_cache"],
+                                    t["v_cache"], o=o, lse=lse, workspace=ws)
+    torch.cuda.synchronize()
+    st: dict[str, list] = {}
+    for ev in evs:
+        for name, ms in ev.elapsed_all():
+            st.setdefault(name, []).append(ms)
+    avg = {k: float(np.mean(v)) for k, v in st.items()}
+    f = 4.0 * p.batch * p.heads * p.Nq * (ks * p.c) * p.head_dim
+    attn = avg.get("attn_fwd_mfma", float("nan"))
+    return {"workload": "720p-class continuation: 12 condition frames cached, top-r=72 noise "
+                        "cubes + own cube + 720 condition cubes",
+            "k_sel": ks, "tflop": round(f / 1e12, 3), "gather_ms": round(avg.get("gather_qkv", 0), 3),
+            "attn_ms": round(attn, 3), "attn_tflops": round(f / (attn * 1e-3) / 1e12, 1),
+            "frac_peak": round(f / (attn * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+
+
+if __name__ == "__main__":
+    sys.exit(main())

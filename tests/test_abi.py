@@ -51,10 +51,16 @@ def test_num_selected_and_workspace(L):
     big = bsa.Problem(1, 32, 128, 24, 48, 80, 4, 4, 4)
     assert bsa.bsa_num_selected(big, 144) == 145
     import torch
+    gathers = 3 * 32 * 1440 * 64 * 128 * 2                           # Q, K rows + V^T, bf16
     fwd = bsa.bsa_workspace_bytes(big, torch.bfloat16, 145, False)
-    assert fwd == 2 * 32 * 1440 * 64 * 128 * 2                      # K rows + V^T, bf16
+    assert fwd > gathers                                             # + key-range partials
+    os.environ["BSA_FWD_SPLITS"] = "1"
+    try:
+        assert bsa.bsa_workspace_bytes(big, torch.bfloat16, 145, False) == gathers
+    finally:
+        del os.environ["BSA_FWD_SPLITS"]
     assert bsa.bsa_workspace_bytes(big, torch.float32, 145, False) == 0
-    assert bsa.bsa_workspace_bytes(big, torch.bfloat16, 145, True) > fwd
+    assert bsa.bsa_workspace_bytes(big, torch.bfloat16, 145, True) > gathers
     with pytest.raises(bsa.BsaError):
         bsa.bsa_workspace_bytes(big, torch.bfloat16, 1441, False)
 

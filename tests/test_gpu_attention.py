@@ -93,6 +93,29 @@ def test_fwd_continuation_small(path):
     assert_close(lse.cpu().numpy(), LSE, "bf16", "LSE", max_abs=2e-3, rel=1e-5)
 
 
+@pytest.mark.parametrize("splits, early", [(2, None), (3, None), (8, "1"), (16, "0"),
+                                           (40, None)])
+def test_fwd_key_range_split(splits, early, monkeypatch):
+    """The key-range split forward (partials + merge) against the oracle, including ranges that
+    hold no selected cube for some query cubes and more ranges than key cubes."""
+    monkeypatch.setenv("BSA_FWD_SPLITS", str(splits))
+    if early is not None:
+        monkeypatch.setenv("BSA_FWD_EARLY_K", early)
+    for number, over, r in ((2, dict(batch=2, heads=2, T=8, H=8, W=32), 5),
+                            (4, dict(heads=2, T=12, H=8, W=16, cond_T=4), 3)):
+        w = synth.workload(number, **over)
+        x = synth.make_inputs(w)
+        print_case(f"fwd split={splits} early={early} {w.name} {over}")
+        p, op, idx, t = _setup(w, x, r)
+        ks = orc.num_selected(op, r)
+        scale = scale_of(op)
+        o, lse = _fwd(p, t, idx, ks, scale)
+        O, LSE = orc.sparse_attn_fwd(x["q"], x["k"], x["v"], x.get("k_cache"), x.get("v_cache"),
+                                     idx, op, scale)
+        assert_close(o.float().cpu().numpy(), O, "bf16", "O")
+        assert_close(lse.cpu().numpy(), LSE, "bf16", "LSE", max_abs=2e-3, rel=1e-5)
+
+
 def _gpu_selection(w, t, p):
     qm = bsa.bsa_block_pool(p, t["q"])
     km = bsa.bsa_block_pool(p, t["k"])

@@ -277,19 +277,22 @@ class StageEvents:
         return self
 
     def __exit__(self, *exc):
-        lib().bsa_set_stage_events(None, 0)
+        L = lib()
+        L.bsa_set_stage_events(None, 0)
+        count = min(L.bsa_stage_count(), self.n - 1)
+        self.names = [L.bsa_stage_name(s).decode() for s in range(max(count, 0))]
         return False
 
-    def elapsed(self):
-        """[(stage name, ms)] for the stages of the last call (synchronises on its last event)."""
-        L = lib()
-        count = min(L.bsa_stage_count(), self.n - 1)
-        if count <= 0:
+    def elapsed_all(self):
+        """[(stage name, ms)] for the stages of the call made inside this `with` block
+        (synchronises on that call's last event)."""
+        names = getattr(self, "names", [])
+        if not names:
             return []
-        self.hip.hipEventSynchronize(self.arr[count])
+        self.hip.hipEventSynchronize(self.arr[len(names)])
         out = []
-        for s in range(count):
+        for s, name in enumerate(names):
             ms = ctypes.c_float()
             self.hip.hipEventElapsedTime(ctypes.byref(ms), self.arr[s], self.arr[s + 1])
-            out.append((L.bsa_stage_name(s).decode(), float(ms.value)))
+            out.append((name, float(ms.value)))
         return out

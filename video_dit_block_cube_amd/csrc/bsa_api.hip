@@ -7,6 +7,7 @@
 // paragraph; "LongCat-Video 高效長視頻生成探索世界模型的第壹步", meituan.com talk, section 2.1),
 // and the backward (same talk, section 2.2).  Every check runs on the host before any HIP call.
 #include <cmath>
+#include <cstdlib>
 #include <cstring>
 #include <exception>
 #include <string>
@@ -130,8 +131,24 @@ BwdWs bwd_layout(const Geom& g, bool mfma, int k_sel) {
   return w;
 }
 
+// Key-range split count of the MFMA forward: BSA_FWD_SPLITS overrides the size-based choice
+// (tuning aid; 1 disables the split).
+int fwd_splits(const Geom& g) {
+  const char* env = std::getenv("BSA_FWD_SPLITS");
+  return fwd_split_ranges(g, env ? std::atoi(env) : -1);
+}
+
+// The query-only view of a problem (no condition segment): gathers of Q cover the noise cubes.
+Geom noise_only(const Geom& g) {
+  return make_geom(g.B, g.Hh, g.D, g.nT, g.H, g.W, g.ct, g.ch, g.cw, 0);
+}
+
+// Forward workspace (MFMA path): K rows + V^T over all nbk key cubes, Q rows over the nbq query
+// cubes, then the key-range partials.
 size_t fwd_ws(const Geom& g, bool mfma) {
-  return mfma ? 2 * align_up(gather_bytes(g, true)) : 0;
+  if (!mfma) return 0;
+  return 2 * align_up(gather_bytes(g, true)) + align_up(gather_bytes(noise_only(g), true)) +
+         align_up(fwd_split_bytes(g, fwd_splits(g)));
 }
 
 template <typename F>
@@ -208,17 +225,26 @@ bsa_status_t bsa_sparse_attn_fwd(const bsa_problem_t* p, bsa_dtype_t dtype, cons
       return fail(BSA_ERR_WORKSPACE, "workspace smaller than bsa_workspace_bytes()");
     Stages stages(stream);
     if (mfma) {
-      bf16_t* krow = static_cast<bf16_t*>(ws);
-      bf16_t* vtr = reinterpret_cast<bf16_t*>(static_cast<char*>(ws) +
-                                              align_up(gather_bytes(g, true)));
+      char* base = static_cast<char*>(ws);
+      const Geom gq = noise_only(g);
+      bf16_t* krow = reinterpret_cast<bf16_t*>(base);
+      bf16_t* vtr = reinterpret_cast<bf16_t*>(base + align_up(gather_bytes(g, true)));
+      bf16_t* qrow = reinterpret_cast<bf16_t*>(base + 2 * align_up(gather_bytes(g, true)));
+      void* split_ws = base + 2 * align_up(gather_bytes(g, true)) +
+                       align_up(gather_bytes(gq, true));
       st = hip_status(launch_gather(g, k, k_cache, GATHER_ROW, krow, nullptr, stream),
                       "gather K");
       if (st != BSA_OK) return st;
       st = hip_status(launch_gather(g, v, v_cache, GATHER_TRANS, nullptr, vtr, stream),
                       "gather V");
       if (st != BSA_OK) return st;
-      stages.done("gather_kv");
-      st = hip_status(launch_fwd_mfma(g, q, krow, vtr, idx, k_sel, softmax_scale, o, lse, stream),
+      st = hip_status(launch_gather(gq, q, nullptr, GATHER_ROW, qrow, nullptr, stream),
+                      "gather Q");
+      if (st != BSA_OK) return st;
+      stages.done("gather_qkv");
+      const int ns = fwd_splits(g);
+      st = hip_status(launch_fwd_mfma(g, qrow, krow, vtr, idx, k_sel, softmax_scale, o, lse, ns,
+                                      split_ws, stream),
                       "attention forward launch");
       stages.done("attn_fwd_mfma");
     } else {

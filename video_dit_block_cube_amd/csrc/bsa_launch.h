@@ -47,10 +47,15 @@ size_t gather_bytes(const Geom& g, bool with_cache);
 hipError_t launch_gather(const Geom& g, const void* x, const void* x_cache, int mode,
                          bf16_t* out_row, bf16_t* out_trans, hipStream_t s);
 
-// k_attn_mfma.hip: bf16 MFMA forward for c == 64, D in {64, 128}.
-hipError_t launch_fwd_mfma(const Geom& g, const void* q, const bf16_t* k_row,
+// k_attn_mfma.hip: bf16 MFMA forward for c == 64, D in {64, 128}; q_row is Q in the ROW gather
+// layout over the nbq query cubes ([B, Hh, nbq, 64*D]).  ns <= 1 runs one pass per
+// query cube; ns > 1 splits the key cube ids into ns ranges (one XCD's L2 per range) and merges
+// the partials, which need fwd_split_bytes(g, ns) bytes of split_ws.
+int fwd_split_ranges(const Geom& g, int requested);
+size_t fwd_split_bytes(const Geom& g, int ns);
+hipError_t launch_fwd_mfma(const Geom& g, const bf16_t* q_row, const bf16_t* k_row,
                            const bf16_t* v_trans, const int32_t* idx, int k_sel, float scale,
-                           void* o, float* lse, hipStream_t s);
+                           void* o, float* lse, int ns, void* split_ws, hipStream_t s);
 
 // k_bwd_mfma.hip: bf16 MFMA backward kernels for c == 64, D in {64, 128}.
 hipError_t launch_bwd_dq_mfma(const Geom& g, const void* q, const void* d_o,

@@ -22,6 +22,8 @@
 //  * Work order is head-major (all XCDs work on the same (b, h) at a time, keeping that head's
 //    K/V hot in the shared Infinity Cache) and XCD-aware: workgroup L runs on XCD L%8, which gets
 //    a contiguous run of query cubes of the head (spatial neighbours select similar key cubes).
+#include <cstdlib>
+
 #include "bsa_launch.h"
 
 namespace bsa {
@@ -42,6 +44,40 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, si
                                            0x00020000);
 }
 
+// Q^T operand fragments straight from the ROW-gathered Q cube into LDS, no VGPRs in between:
+// instruction (s, qb) moves the 1 KB block of lanes' 16-byte fragments to qs[(s*2 + qb)*64 ...].
+template <int D>
+__device__ __forceinline__ void load_q_lds(__amdgpu_buffer_rsrc_t rq, int qoff, bf16x8* qs,
+                                           int lane) {
+  constexpr int S = D / 16;
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+    for (int s = 0; s < S; ++s)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rq, (__attribute__((address_space(3))) void*)(qs + (s * 2 + qb) * 64), 16, lane * 16,
+          qoff + (qb * S + s) * 1024, 0, 0);
+}
+
+__device__ __forceinline__ void wait_vmem_all() {
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): every vector memory load of this wave is done
+}
+
+// [lo, hi) = positions of the ascending selection row whose cube ids lie in [key_lo, key_hi),
+// counted with one coalesced pass over the row.
+__device__ __forceinline__ void row_span(const int32_t* __restrict__ irow, int k_sel, int key_lo,
+                                         int key_hi, int lane, int& lo, int& hi) {
+  int below_lo = 0, below_hi = 0;
+  for (int c0 = 0; c0 < k_sel; c0 += 64) {
+    const int e = c0 + lane;
+    const int v = e < k_sel ? irow[e] : 0x7fffffff;
+    below_lo += __popcll(__ballot(v < key_lo));
+    below_hi += __popcll(__ballot(v < key_hi));
+  }
+  lo = below_lo;
+  hi = below_hi;
+}
+
 __device__ __forceinline__ bf16x8 pack8(const f32x16& a, int base) {
   bf16x8 r;
 #pragma unroll
@@ -51,66 +87,30 @@ __device__ __forceinline__ bf16x8 pack8(const f32x16& a, int base) {
 
 }  // namespace
 
-template <int D>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_mfma_kernel(Geom g, const bf16_t* __restrict__ q,
-                                                      const bf16_t* __restrict__ krow,
-                                                      const bf16_t* __restrict__ vtr,
-                                                      const int32_t* __restrict__ idx, int k_sel,
-                                                      float c_log2, int cpx,
-                                                      bf16_t* __restrict__ o,
-                                                      float* __restrict__ lse) {
-  constexpr int S = D / 16;   // k-steps of the QK^T contraction
-  constexpr int DB = D / 32;  // 32-row blocks of O^T
-  __shared__ bf16x8 qs[S * 2 * 64];
-
-  const int L = blockIdx.x;
-  const int xcd = L & 7;
-  const int k8 = L >> 3;
-  const int bh = k8 / cpx;
-  const int i = xcd * cpx + (k8 % cpx);
-  if (i >= g.nbq) return;
-  const int b = bh / g.Hh, h = bh % g.Hh;
-  const int lane = threadIdx.x;
-  const int l32 = lane & 31;
-  const int hh = lane >> 5;
-
-  // Q^T operand fragments -> LDS (each lane stores exactly what it will read back).
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const int tq = cube_token(g, i, 32 * qb + l32);
-    const bf16_t* src = q + bnhd_offset(g, g.Nq, b, tq, h) + hh * (D / 2);
-#pragma unroll
-    for (int s = 0; s < S; ++s) qs[(s * 2 + qb) * 64 + lane] = ld16(src + 8 * s);
-  }
-
-  f32x16 acc[DB][2];
-#pragma unroll
-  for (int db = 0; db < DB; ++db)
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[db][qb][e] = 0.f;
-  float m_run[2] = {-INFINITY, -INFINITY};
-  float l_part[2] = {0.f, 0.f};
-
-  const int32_t* irow = idx + ((size_t)bh * g.nbq + i) * k_sel;
+// Online-softmax attention of one 64-token query cube over the 32-key half cubes
+// [t_begin, t_end) of its (ascending) selection row.  Accumulates O^T (unnormalised), the running
+// base-2 max and this lane's partial row sums.
+template <int D, bool EARLY_K>
+__device__ __forceinline__ void attend_span(const bf16x8* __restrict__ qs,
+                                            __amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv,
+                                            const int32_t* __restrict__ irow, int t_begin,
+                                            int t_end, float c_log2, int lane,
+                                            f32x16 (&acc)[D / 32][2], float (&m_run)[2],
+                                            float (&l_part)[2]) {
+  constexpr int S = D / 16;
+  constexpr int DB = D / 32;
   constexpr int cube_bytes = 64 * D * 2;
-  const size_t bh_bytes = (size_t)g.nbk * cube_bytes;
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(krow + (size_t)bh * g.nbk * (64 * D), bh_bytes);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(vtr + (size_t)bh * g.nbk * (64 * D), bh_bytes);
   const int vlane = lane * 16;
-  const int ntiles = 2 * k_sel;
-
   bf16x8 kr[S], vr[DB * 2];
   {
-    const int off0 = irow[0] * cube_bytes;
+    const int off0 = irow[t_begin >> 1] * cube_bytes + (t_begin & 1) * (32 * D * 2);
 #pragma unroll
     for (int s = 0; s < S; ++s) kr[s] = bld16(rk, vlane, off0 + s * 1024);
 #pragma unroll
     for (int u = 0; u < DB * 2; ++u) vr[u] = bld16(rv, vlane, off0 + u * 1024);
   }
-
-  for (int t = 0; t < ntiles; ++t) {
+  wait_vmem_all();  // Q^T fragments were written to LDS by buffer loads issued before these
+  for (int t = t_begin; t < t_end; ++t) {
     // Q^T lives in LDS, not registers: keep the compiler from hoisting its loop-invariant reads.
     asm volatile("" ::: "memory");
     // ---- S^T = K Q^T for this 32-key half cube ----
@@ -126,11 +126,13 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
       st[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr[s], q0, st[0], 0, 0, 0);
       st[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr[s], q1, st[1], 0, 0, 0);
     }
-    // ---- request next tile's K ----
-    const int tn = t + 1 < ntiles ? t + 1 : t;
+    const int tn = t + 1 < t_end ? t + 1 : t;
     const int noff = irow[tn >> 1] * cube_bytes + (tn & 1) * (32 * D * 2);
+    if constexpr (EARLY_K) {
+      // ---- request next tile's K now (longer lead, more live registers) ----
 #pragma unroll
-    for (int s = 0; s < S; ++s) kr[s] = bld16(rk, vlane, noff + s * 1024);
+      for (int s = 0; s < S; ++s) kr[s] = bld16(rk, vlane, noff + s * 1024);
+    }
 
     // ---- online softmax (base 2) ----
     float tgt[2];
@@ -157,37 +159,78 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
           for (int e = 0; e < 16; ++e) acc[db][qb][e] *= alpha;
       }
     }
-    bf16x8 pb[2][2];
+    // ---- P^T (bf16, in place of S^T) and O^T += V^T P^T, one 16-key half at a time ----
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      float ls = 0.f;
+    for (int s2 = 0; s2 < 2; ++s2) {
+      bf16x8 pb[2];
 #pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
+      for (int qb = 0; qb < 2; ++qb) {
+        float ls = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const float p = fast_exp2(fmaf(st[qb][8 * s2 + e], c_log2, -m_run[qb]));
           ls += p;
-          pb[s2][qb][e] = (__bf16)p;
+          pb[qb][e] = (__bf16)p;
         }
+        l_part[qb] += ls;
       }
-      l_part[qb] += ls;
-    }
-
-    // ---- O^T += V^T P^T ----
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2)
+      for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb)
-          acc[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vr[db * 2 + s2], pb[s2][qb],
+          acc[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vr[db * 2 + s2], pb[qb],
                                                                 acc[db][qb], 0, 0, 0);
-    // ---- request next tile's V ----
+    }
+    // ---- request next tile's V (and K when not requested earlier) ----
+    if constexpr (!EARLY_K) {
+#pragma unroll
+      for (int s = 0; s < S; ++s) kr[s] = bld16(rk, vlane, noff + s * 1024);
+    }
 #pragma unroll
     for (int u = 0; u < DB * 2; ++u) vr[u] = bld16(rv, vlane, noff + u * 1024);
   }
+}
 
-  // ---- epilogue: normalise, write O (bf16) and LSE ----
+template <int D>
+__device__ __forceinline__ void zero_acc(f32x16 (&acc)[D / 32][2]) {
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[db][qb][e] = 0.f;
+}
+
+// Single pass: one wave per query cube over its whole selection; writes O (bf16) and LSE.
+template <int D, bool EARLY_K>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_mfma_kernel(
+    Geom g, const bf16_t* __restrict__ q_row, const bf16_t* __restrict__ krow,
+    const bf16_t* __restrict__ vtr, const int32_t* __restrict__ idx, int k_sel, float c_log2,
+    int cpx, bf16_t* __restrict__ o, float* __restrict__ lse) {
+  constexpr int DB = D / 32;
+  constexpr int cube_bytes = 64 * D * 2;
+  __shared__ bf16x8 qs[(D / 16) * 2 * 64];
+  const int L = blockIdx.x;
+  const int xcd = L & 7;
+  const int k8 = L >> 3;
+  const int bh = k8 / cpx;
+  const int i = xcd * cpx + (k8 % cpx);
+  if (i >= g.nbq) return;
+  const int b = bh / g.Hh, h = bh % g.Hh;
+  const int lane = threadIdx.x;
+  const int l32 = lane & 31, hh = lane >> 5;
+  const __amdgpu_buffer_rsrc_t rq =
+      make_rsrc(q_row + (size_t)bh * g.nbq * (64 * D), (size_t)g.nbq * cube_bytes);
+  load_q_lds<D>(rq, i * cube_bytes, qs, lane);
+  const size_t bh_bytes = (size_t)g.nbk * cube_bytes;
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(krow + (size_t)bh * g.nbk * (64 * D), bh_bytes);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(vtr + (size_t)bh * g.nbk * (64 * D), bh_bytes);
+  const int32_t* irow = idx + ((size_t)bh * g.nbq + i) * k_sel;
+  f32x16 acc[DB][2];
+  zero_acc<D>(acc);
+  float m_run[2] = {-INFINITY, -INFINITY};
+  float l_part[2] = {0.f, 0.f};
+  attend_span<D, EARLY_K>(qs, rk, rv, irow, 0, 2 * k_sel, c_log2, lane, acc, m_run, l_part);
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     const float l = l_part[qb] + __shfl_xor(l_part[qb], 32, 64);
@@ -195,7 +238,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     const int tq = cube_token(g, i, 32 * qb + l32);
     bf16_t* orow = o + bnhd_offset(g, g.Nq, b, tq, h);
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
         const int d = 32 * db + 8 * r4 + 4 * hh;
@@ -205,24 +248,196 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
                       ((uint32_t)f32_to_bf16_bits(acc[db][qb][4 * r4 + 3] * inv) << 16);
         *reinterpret_cast<uint2*>(orow + d) = make_uint2(w0, w1);
       }
-    }
     if (hh == 0) lse[(size_t)bh * g.Nq + tq] = (m_run[qb] + fast_log2(l)) * kLn2;
   }
 }
 
-hipError_t launch_fwd_mfma(const Geom& g, const void* q, const bf16_t* k_row,
-                           const bf16_t* v_trans, const int32_t* idx, int k_sel, float scale,
-                           void* o, float* lse, hipStream_t s) {
-  const int cpx = (g.nbq + 7) / 8;
-  dim3 grid((unsigned)(g.B * g.Hh * cpx * 8));
-  const float c_log2 = scale * kLog2e;
-  if (g.D == 64)
-    hipLaunchKernelGGL(fwd_mfma_kernel<64>, grid, dim3(64), 0, s, g, (const bf16_t*)q, k_row,
-                       v_trans, idx, k_sel, c_log2, cpx, (bf16_t*)o, lse);
-  else
-    hipLaunchKernelGGL(fwd_mfma_kernel<128>, grid, dim3(64), 0, s, g, (const bf16_t*)q, k_row,
-                       v_trans, idx, k_sel, c_log2, cpx, (bf16_t*)o, lse);
+// Split over key ranges: key cube ids are cut into NS contiguous ranges of `rc` cubes; work item
+// (range s, b, h, query cube i) attends only the selected cubes of range s and writes a normalised
+// partial O (bf16, [64][D] row-major) plus its base-2 max and row sum.  Range s runs on XCD s%8,
+// whose L2 then only ever holds that range of the head's K/V; the XCD takes its ranges one after
+// the other (s = xcd, xcd + 8, ...), heads in order within each.
+template <int D, bool EARLY_K>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_split_kernel(
+    Geom g, const bf16_t* __restrict__ q_row, const bf16_t* __restrict__ krow,
+    const bf16_t* __restrict__ vtr, const int32_t* __restrict__ idx, int k_sel, float c_log2,
+    int ns, int rc, bf16_t* __restrict__ o_part, float2* __restrict__ ml_part) {
+  constexpr int DB = D / 32;
+  constexpr int cube_bytes = 64 * D * 2;
+  __shared__ bf16x8 qs[(D / 16) * 2 * 64];
+  const int L = blockIdx.x;
+  const int xcd = L & 7;
+  const int k8 = L >> 3;
+  const int per_pass = g.B * g.Hh * g.nbq;
+  const int pass = k8 / per_pass;
+  const int rem = k8 % per_pass;
+  const int bh = rem / g.nbq;
+  const int i = rem % g.nbq;
+  const int sr = xcd + 8 * pass;
+  if (sr >= ns) return;
+  const int b = bh / g.Hh, h = bh % g.Hh;
+  const int lane = threadIdx.x;
+  const int l32 = lane & 31, hh = lane >> 5;
+  const int32_t* irow = idx + ((size_t)bh * g.nbq + i) * k_sel;
+  int lo, hi;
+  row_span(irow, k_sel, sr * rc, (sr + 1) * rc, lane, lo, hi);
+  const size_t item = ((size_t)sr * g.B * g.Hh + bh) * g.nbq + i;
+  float2* ml = ml_part + item * 64;
+  if (lo == hi) {
+    if (hh == 0) {
+      ml[l32] = make_float2(-INFINITY, 0.f);
+      ml[32 + l32] = make_float2(-INFINITY, 0.f);
+    }
+    return;
+  }
+  const __amdgpu_buffer_rsrc_t rq =
+      make_rsrc(q_row + (size_t)bh * g.nbq * (64 * D), (size_t)g.nbq * cube_bytes);
+  load_q_lds<D>(rq, i * cube_bytes, qs, lane);
+  const size_t bh_bytes = (size_t)g.nbk * cube_bytes;
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(krow + (size_t)bh * g.nbk * (64 * D), bh_bytes);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(vtr + (size_t)bh * g.nbk * (64 * D), bh_bytes);
+  f32x16 acc[DB][2];
+  zero_acc<D>(acc);
+  float m_run[2] = {-INFINITY, -INFINITY};
+  float l_part[2] = {0.f, 0.f};
+  attend_span<D, EARLY_K>(qs, rk, rv, irow, 2 * lo, 2 * hi, c_log2, lane, acc, m_run, l_part);
+  bf16_t* op = o_part + item * (64 * D);
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const float l = l_part[qb] + __shfl_xor(l_part[qb], 32, 64);
+    const float inv = 1.0f / l;
+    const int row = 32 * qb + l32;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int d = 32 * db + 8 * r4 + 4 * hh;
+        uint32_t w0 = (uint32_t)f32_to_bf16_bits(acc[db][qb][4 * r4 + 0] * inv) |
+                      ((uint32_t)f32_to_bf16_bits(acc[db][qb][4 * r4 + 1] * inv) << 16);
+        uint32_t w1 = (uint32_t)f32_to_bf16_bits(acc[db][qb][4 * r4 + 2] * inv) |
+                      ((uint32_t)f32_to_bf16_bits(acc[db][qb][4 * r4 + 3] * inv) << 16);
+        *reinterpret_cast<uint2*>(op + row * D + d) = make_uint2(w0, w1);
+      }
+    if (hh == 0) ml[row] = make_float2(m_run[qb], l);
+  }
+}
+
+// Merge of the range partials of one query cube: O = sum_s w_s O_s / sum_s w_s with
+// w_s = l_s * 2^(m_s - M), M = max_s m_s; LSE = (M + log2 sum_s w_s) * ln 2.
+template <int D>
+__global__ __launch_bounds__(256) void fwd_merge_kernel(Geom g, int ns,
+                                                        const bf16_t* __restrict__ o_part,
+                                                        const float2* __restrict__ ml_part,
+                                                        bf16_t* __restrict__ o,
+                                                        float* __restrict__ lse) {
+  constexpr int DQ = D / 4;  // columns per thread
+  const int i = blockIdx.x;
+  const int bh = blockIdx.y;
+  const int b = bh / g.Hh, h = bh % g.Hh;
+  const int t = threadIdx.x;
+  const int row = t >> 2, part = t & 3;
+  const size_t per_s = (size_t)g.B * g.Hh * g.nbq;
+  float M = -INFINITY;
+  for (int s = 0; s < ns; ++s) {
+    const float2 v = ml_part[(s * per_s + (size_t)bh * g.nbq + i) * 64 + row];
+    if (v.y > 0.f) M = fmaxf(M, v.x);
+  }
+  float acc[DQ];
+#pragma unroll
+  for (int e = 0; e < DQ; ++e) acc[e] = 0.f;
+  float Lsum = 0.f;
+  for (int s = 0; s < ns; ++s) {
+    const size_t item = s * per_s + (size_t)bh * g.nbq + i;
+    const float2 v = ml_part[item * 64 + row];
+    if (!(v.y > 0.f)) continue;
+    const float w = v.y * fast_exp2(v.x - M);
+    Lsum += w;
+    const uint4* src = reinterpret_cast<const uint4*>(o_part + item * (64 * D) + row * D + part * DQ);
+#pragma unroll
+    for (int c8 = 0; c8 < DQ / 8; ++c8) {
+      const uint4 u = src[c8];
+      const uint32_t wd[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        acc[c8 * 8 + 2 * k] = fmaf(w, __uint_as_float(wd[k] << 16), acc[c8 * 8 + 2 * k]);
+        acc[c8 * 8 + 2 * k + 1] = fmaf(w, __uint_as_float(wd[k] & 0xFFFF0000u), acc[c8 * 8 + 2 * k + 1]);
+      }
+    }
+  }
+  const float inv = 1.0f / Lsum;
+  const int tok = cube_token(g, i, row);
+  bf16_t* orow = o + bnhd_offset(g, g.Nq, b, tok, h) + part * DQ;
+#pragma unroll
+  for (int c8 = 0; c8 < DQ / 8; ++c8) {
+    uint32_t wd[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      wd[k] = (uint32_t)f32_to_bf16_bits(acc[c8 * 8 + 2 * k] * inv) |
+              ((uint32_t)f32_to_bf16_bits(acc[c8 * 8 + 2 * k + 1] * inv) << 16);
+    reinterpret_cast<uint4*>(orow)[c8] = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+  }
+  if (part == 0) lse[(size_t)bh * g.Nq + tok] = (M + fast_log2(Lsum)) * kLn2;
+}
+
+size_t fwd_split_bytes(const Geom& g, int ns) {
+  if (ns <= 1) return 0;
+  const size_t items = (size_t)ns * g.B * g.Hh * g.nbq;
+  return items * 64 * g.D * sizeof(bf16_t) + items * 64 * sizeof(float2) + 256;
+}
+
+int fwd_split_ranges(const Geom& g, int requested) {
+  if (requested >= 0) return requested <= 1 ? 1 : requested;
+  // Split when one head's gathered K/V (32 KB per cube) is far larger than one XCD's 4 MB L2.
+  const double head_kv = (double)g.nbk * 64 * g.D * 2 * 2;
+  return head_kv > 8.0 * (1 << 20) ? 8 : 1;
+}
+
+template <int D, bool EK>
+static hipError_t launch_fwd_t(const Geom& g, const bf16_t* q_row, const bf16_t* k_row,
+                               const bf16_t* v_trans, const int32_t* idx, int k_sel,
+                               float c_log2, void* o, float* lse, int ns, void* split_ws,
+                               hipStream_t s) {
+  if (ns <= 1) {
+    const int cpx = (g.nbq + 7) / 8;
+    dim3 grid((unsigned)(g.B * g.Hh * cpx * 8));
+    hipLaunchKernelGGL((fwd_mfma_kernel<D, EK>), grid, dim3(64), 0, s, g, q_row,
+                       k_row, v_trans, idx, k_sel, c_log2, cpx, (bf16_t*)o, lse);
+    return hipGetLastError();
+  }
+  const int rc = (g.nbk + ns - 1) / ns;
+  const size_t items = (size_t)ns * g.B * g.Hh * g.nbq;
+  bf16_t* o_part = static_cast<bf16_t*>(split_ws);
+  float2* ml_part = reinterpret_cast<float2*>(o_part + items * 64 * g.D);
+  const int passes = (ns + 7) / 8;
+  dim3 grid((unsigned)(8 * passes * g.B * g.Hh * g.nbq));
+  hipLaunchKernelGGL((fwd_split_kernel<D, EK>), grid, dim3(64), 0, s, g, q_row,
+                     k_row, v_trans, idx, k_sel, c_log2, ns, rc, o_part, ml_part);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  dim3 mgrid(g.nbq, g.B * g.Hh);
+  hipLaunchKernelGGL(fwd_merge_kernel<D>, mgrid, dim3(256), 0, s, g, ns, o_part, ml_part,
+                     (bf16_t*)o, lse);
   return hipGetLastError();
+}
+
+hipError_t launch_fwd_mfma(const Geom& g, const bf16_t* q_row, const bf16_t* k_row,
+                           const bf16_t* v_trans, const int32_t* idx, int k_sel, float scale,
+                           void* o, float* lse, int ns, void* split_ws, hipStream_t s) {
+  const float c_log2 = scale * kLog2e;
+  // Next-K request right after the S MFMAs needs ~30 more VGPRs; D = 128 has no room for them
+  // at two waves per SIMD, so there it is requested together with V (tuning override:
+  // BSA_FWD_EARLY_K=0/1).
+  const char* env = std::getenv("BSA_FWD_EARLY_K");
+  const bool early = env ? std::atoi(env) != 0 : g.D == 64;
+  if (g.D == 64)
+    return early ? launch_fwd_t<64, true>(g, q_row, k_row, v_trans, idx, k_sel, c_log2, o, lse, ns,
+                                          split_ws, s)
+                 : launch_fwd_t<64, false>(g, q_row, k_row, v_trans, idx, k_sel, c_log2, o, lse, ns,
+                                           split_ws, s);
+  return early ? launch_fwd_t<128, true>(g, q_row, k_row, v_trans, idx, k_sel, c_log2, o, lse, ns,
+                                         split_ws, s)
+               : launch_fwd_t<128, false>(g, q_row, k_row, v_trans, idx, k_sel, c_log2, o, lse, ns,
+                                          split_ws, s);
 }
 
 }  // namespace bsa
