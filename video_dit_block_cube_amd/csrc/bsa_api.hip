@@ -100,7 +100,7 @@ bsa_status_t hip_status(hipError_t e, const char* what) {
 
 // Workspace layout of the backward (and of the forward for the MFMA path).
 struct BwdWs {
-  size_t delta, lse, bits, off, list, g_qr, g_qt, g_dr, g_dt, g_kr, g_kt, g_vr, total;
+  size_t delta, lse, ld, bits, off, list, g_qr, g_dr, g_kr, g_vr, total;
 };
 
 BwdWs bwd_layout(const Geom& g, bool mfma, int k_sel) {
@@ -114,17 +114,15 @@ BwdWs bwd_layout(const Geom& g, bool mfma, int k_sel) {
   const size_t per_cube = (size_t)g.B * g.Hh * g.nbq * g.c * sizeof(float);
   w.delta = take(per_cube);
   w.lse = take(per_cube);
+  w.ld = take(2 * per_cube);
   w.bits = take(csr_bits_words(g) * sizeof(uint32_t));
   w.off = take((size_t)g.B * g.Hh * (g.nbk + 1) * sizeof(int32_t));
   w.list = take((size_t)g.B * g.Hh * g.nbq * (size_t)k_sel * sizeof(int32_t));
   if (mfma) {
     const size_t gb = gather_bytes(g, true);
     w.g_qr = take(gb);
-    w.g_qt = take(gb);
     w.g_dr = take(gb);
-    w.g_dt = take(gb);
     w.g_kr = take(gb);
-    w.g_kt = take(gb);
     w.g_vr = take(gb);
   }
   w.total = at;
@@ -285,33 +283,35 @@ bsa_status_t bsa_sparse_attn_bwd(const bsa_problem_t* p, bsa_dtype_t dtype, cons
     int32_t* list = reinterpret_cast<int32_t*>(base + w.list);
     const bool bf16 = dtype == BSA_BF16;
     Stages stages(stream);
-    st = hip_status(launch_delta(g, bf16, o, d_o, lse, delta_c, lse_c, stream), "delta launch");
+    float2* ld_c = reinterpret_cast<float2*>(base + w.ld);
+    st = hip_status(launch_delta(g, bf16, o, d_o, lse, delta_c, lse_c, ld_c, stream),
+                    "delta launch");
     if (st != BSA_OK) return st;
     st = hip_status(launch_csr(g, idx, k_sel, bits, off, list, stream), "csr launch");
     if (st != BSA_OK) return st;
     stages.done("bwd_prep");
     if (mfma) {
       auto at = [&](size_t o2) { return reinterpret_cast<bf16_t*>(base + o2); };
-      st = hip_status(launch_gather(g, q, nullptr, GATHER_ROW | GATHER_TRANS, at(w.g_qr),
-                                    at(w.g_qt), stream), "gather Q");
+      st = hip_status(launch_gather(g, q, nullptr, GATHER_ROW, at(w.g_qr), nullptr, stream),
+                      "gather Q");
       if (st != BSA_OK) return st;
-      st = hip_status(launch_gather(g, d_o, nullptr, GATHER_ROW | GATHER_TRANS, at(w.g_dr),
-                                    at(w.g_dt), stream), "gather dO");
+      st = hip_status(launch_gather(g, d_o, nullptr, GATHER_ROW, at(w.g_dr), nullptr, stream),
+                      "gather dO");
       if (st != BSA_OK) return st;
-      st = hip_status(launch_gather(g, k, nullptr, GATHER_ROW | GATHER_TRANS, at(w.g_kr),
-                                    at(w.g_kt), stream), "gather K");
+      st = hip_status(launch_gather(g, k, nullptr, GATHER_ROW, at(w.g_kr), nullptr, stream),
+                      "gather K");
       if (st != BSA_OK) return st;
       st = hip_status(launch_gather(g, v, nullptr, GATHER_ROW, at(w.g_vr), nullptr, stream),
                       "gather V");
       if (st != BSA_OK) return st;
       stages.done("gather_qkv_do");
-      st = hip_status(launch_bwd_dkdv_mfma(g, k, v, at(w.g_qr), at(w.g_qt), at(w.g_dr),
-                                           at(w.g_dt), lse_c, delta_c, off, list,
-                                           softmax_scale, dk, dv, stream), "dK/dV launch");
+      st = hip_status(launch_bwd_dkdv_mfma(g, at(w.g_kr), at(w.g_vr), at(w.g_qr), at(w.g_dr),
+                                           ld_c, off, list, softmax_scale, dk, dv, stream),
+                      "dK/dV launch");
       if (st != BSA_OK) return st;
       stages.done("bwd_dkdv_mfma");
-      st = hip_status(launch_bwd_dq_mfma(g, q, d_o, at(w.g_kr), at(w.g_kt), at(w.g_vr), lse_c,
-                                         delta_c, idx, k_sel, softmax_scale, dq, stream),
+      st = hip_status(launch_bwd_dq_mfma(g, at(w.g_qr), at(w.g_dr), at(w.g_kr), at(w.g_vr),
+                                         ld_c, idx, k_sel, softmax_scale, dq, stream),
                       "dQ launch");
       stages.done("bwd_dq_mfma");
     } else {

@@ -31,9 +31,11 @@ hipError_t launch_bwd_dkdv_simt(const Geom& g, bool bf16, const void* q, const v
                                 const int32_t* csr_list, float scale, float* dk, float* dv,
                                 hipStream_t s);
 
-// k_bwd_prep.hip: Delta and LSE in cube order ([B, Hh, nbq, c]) and the CSR transpose of idx.
+// k_bwd_prep.hip: Delta and LSE in cube order ([B, Hh, nbq, c]) and the CSR transpose of idx;
+// ld_c (may be NULL) additionally receives the interleaved (LSE, Delta) pairs.
 hipError_t launch_delta(const Geom& g, bool bf16, const void* o, const void* d_o,
-                        const float* lse, float* delta_c, float* lse_c, hipStream_t s);
+                        const float* lse, float* delta_c, float* lse_c, float2* ld_c,
+                        hipStream_t s);
 size_t csr_bits_words(const Geom& g);
 hipError_t launch_csr(const Geom& g, const int32_t* idx, int k_sel, uint32_t* bits,
                       int32_t* csr_off, int32_t* csr_list, hipStream_t s);
@@ -57,15 +59,14 @@ hipError_t launch_fwd_mfma(const Geom& g, const bf16_t* q_row, const bf16_t* k_r
                            const bf16_t* v_trans, const int32_t* idx, int k_sel, float scale,
                            void* o, float* lse, int ns, void* split_ws, hipStream_t s);
 
-// k_bwd_mfma.hip: bf16 MFMA backward kernels for c == 64, D in {64, 128}.
-hipError_t launch_bwd_dq_mfma(const Geom& g, const void* q, const void* d_o,
-                              const bf16_t* k_row, const bf16_t* k_trans, const bf16_t* v_row,
-                              const float* lse_c, const float* delta_c, const int32_t* idx,
-                              int k_sel, float scale, float* dq, hipStream_t s);
-hipError_t launch_bwd_dkdv_mfma(const Geom& g, const void* k, const void* v,
-                                const bf16_t* q_row, const bf16_t* q_trans,
-                                const bf16_t* do_row, const bf16_t* do_trans,
-                                const float* lse_c, const float* delta_c,
+// k_bwd_mfma.hip: bf16 MFMA backward kernels for c == 64, D in {64, 128}; every operand comes
+// from the ROW gather layout (transposed operands are read from LDS with ds_read_b64_tr_b16).
+hipError_t launch_bwd_dq_mfma(const Geom& g, const bf16_t* q_row, const bf16_t* do_row,
+                              const bf16_t* k_row, const bf16_t* v_row, const float2* ld_c,
+                              const int32_t* idx, int k_sel, float scale, float* dq,
+                              hipStream_t s);
+hipError_t launch_bwd_dkdv_mfma(const Geom& g, const bf16_t* k_row, const bf16_t* v_row,
+                                const bf16_t* q_row, const bf16_t* do_row, const float2* ld_c,
                                 const int32_t* csr_off, const int32_t* csr_list, float scale,
                                 float* dk, float* dv, hipStream_t s);
 

@@ -44,20 +44,75 @@ __device__ __forceinline__ void zero16(f32x16& a) {
 }  // namespace
 
 // ---------------------------------------------------------------------------------------------
-// dQ: grid = B*Hh*cpx*8 (head-major, XCD-aware like the forward), one wave per query cube.
+// Shared LDS helpers.
+// ---------------------------------------------------------------------------------------------
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) char lds_char;
+
+// Operand fragment of a ROW-layout 32-row half block staged in LDS: lane's 16 bytes of step s.
+__device__ __forceinline__ bf16x8 lds_row_frag(const lds_char* stage, int lane, int s) {
+  return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(stage + (s * 64 + lane) * 16);
+}
+
+// Byte offset (inside a staged ROW half block) of lane's transposed read for operand (db, s2),
+// half eh: ds_read_b64_tr_b16 gives lane m of each 16-lane group g element k of
+// v[4k + m/4][m%4], where v[n] is the 4-element run at lane n's address.  Pointing lane n at
+// row 16*s2 + 8*eh + 4*(g/2) + n/4, columns d = 32*db + 16*(g%2) + 4*(n%4) .. +3 turns the run
+// into the TRANS operand (lane = d, 8 rows in accumulator-row order).
+__device__ __forceinline__ int tr_lane_base(int lane) {
+  const int g = lane >> 4, n = lane & 15;
+  // ROW element (row r, column d) sits at ((s'*64 + lane')*8 + e')*2 with lane' = (d/64)*32 + r,
+  // s' = (d%64)/8, e' = d%8; the lane-dependent part:
+  return ((128 * (g & 1) + 64 * ((n & 3) >> 1) + 4 * (g >> 1) + (n >> 2)) * 8 + 4 * (n & 1)) * 2;
+}
+// The row-split point of the ROW layout is d = D/2: column d lives at lane' = (d/(D/2))*32 + r,
+// step s' = (d%(D/2))/8.  With d = 32*db + (lane part), that gives per-(db, s2, eh) constants:
+template <int D>
+__device__ __forceinline__ int tr_const(int db, int s2, int eh) {
+  if constexpr (D == 128) return ((256 * (db & 1) + 32 * (db >> 1) + 16 * s2 + 8 * eh) * 8) * 2;
+  else return ((32 * db + 16 * s2 + 8 * eh) * 8) * 2;  // D == 64
+}
+template <int D>
+__device__ __forceinline__ bf16x8 lds_trans_frag(const lds_char* stage, int lane_base, int db,
+                                                 int s2) {
+  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4i16*)(stage + lane_base + tr_const<D>(db, s2, 0)));
+  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4i16*)(stage + lane_base + tr_const<D>(db, s2, 1)));
+  typedef short v8i16 __attribute__((ext_vector_type(8)));
+  const v8i16 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, both);
+}
+
+// One 32-row half block (S*1 KB) of a ROW-gathered tensor -> LDS, no VGPRs in between.
+template <int D>
+__device__ __forceinline__ void stage_half(__amdgpu_buffer_rsrc_t r, int soff, lds_char* dst,
+                                           int lane) {
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(dst + s * 1024),
+                                             16, lane * 16, soff + s * 1024, 0, 0);
+}
+
+// ---------------------------------------------------------------------------------------------
+// dQ (query-stationary): grid = B*Hh*cpx*8, one wave per query cube.  Per 32-key half cube:
+// K and V rows are staged straight into LDS (double buffered, the next tile in flight while this
+// one computes), S^T = K Q^T and dP^T = V dO^T take the K/V rows as A operands and Q, dO rows
+// (held in registers) as B operands; dS^T stays in the accumulator registers and, as bf16, is
+// the B operand of dQ^T += K^T dS^T, whose A operand is read transposed from the staged K rows.
 // ---------------------------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(64) void bwd_dq_mfma_kernel(
-    Geom g, const bf16_t* __restrict__ q, const bf16_t* __restrict__ d_o,
-    const bf16_t* __restrict__ k_row, const bf16_t* __restrict__ k_trans,
-    const bf16_t* __restrict__ v_row, const float* __restrict__ lse_c,
-    const float* __restrict__ delta_c, const int32_t* __restrict__ idx, int k_sel, float scale,
+    Geom g, const bf16_t* __restrict__ q_row, const bf16_t* __restrict__ do_row,
+    const bf16_t* __restrict__ k_row, const bf16_t* __restrict__ v_row,
+    const float2* __restrict__ ld_c, const int32_t* __restrict__ idx, int k_sel, float scale,
     float c_log2, int cpx, float* __restrict__ dq) {
   constexpr int S = D / 16;
   constexpr int DB = D / 32;
   constexpr int cube_bytes = 64 * D * 2;
-  __shared__ bf16x8 qs[S * 2 * 64];
-  __shared__ bf16x8 dos[S * 2 * 64];
+  constexpr int half_bytes = 32 * D * 2;
+  __shared__ __attribute__((aligned(16))) char stage0[2 * half_bytes];  // K rows | V rows
+  __shared__ __attribute__((aligned(16))) char stage1[2 * half_bytes];
 
   const int L = blockIdx.x;
   const int xcd = L & 7;
@@ -70,71 +125,75 @@ __global__ __launch_bounds__(64) void bwd_dq_mfma_kernel(
   const int l32 = lane & 31;
   const int hh = lane >> 5;
 
+  const size_t bh_bytes = (size_t)g.nbk * cube_bytes;
+  const size_t bh_elems = (size_t)g.nbk * 64 * D;
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(k_row + bh * bh_elems, bh_bytes);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(v_row + bh * bh_elems, bh_bytes);
+  const int32_t* irow = idx + ((size_t)bh * g.nbq + i) * k_sel;
+  const int ntiles = 2 * k_sel;
+  lds_char* st0 = (lds_char*)stage0;
+  lds_char* st1 = (lds_char*)stage1;
+  {
+    const int off0 = irow[0] * cube_bytes;
+    stage_half<D>(rk, off0, st0, lane);
+    stage_half<D>(rv, off0, st0 + half_bytes, lane);
+  }
+
+  // Q and dO rows of this query cube as B operands (lane = query, 8 consecutive d).
+  const size_t q_bh = (size_t)bh * g.nbq * (64 * D);
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(q_row + q_bh, (size_t)g.nbq * cube_bytes);
+  const __amdgpu_buffer_rsrc_t rd = make_rsrc(do_row + q_bh, (size_t)g.nbq * cube_bytes);
+  bf16x8 qreg[2][S], dreg[2][S];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      qreg[qb][s] = bld16(rq, lane * 16, i * cube_bytes + (qb * S + s) * 1024);
+      dreg[qb][s] = bld16(rd, lane * 16, i * cube_bytes + (qb * S + s) * 1024);
+    }
   float lse2[2], dl[2];
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
-    const int tq = cube_token(g, i, 32 * qb + l32);
-    const size_t off = bnhd_offset(g, g.Nq, b, tq, h) + hh * (D / 2);
-#pragma unroll
-    for (int s = 0; s < S; ++s) {
-      qs[(s * 2 + qb) * 64 + lane] = ld16g(q + off + 8 * s);
-      dos[(s * 2 + qb) * 64 + lane] = ld16g(d_o + off + 8 * s);
-    }
-    const size_t ci = ((size_t)bh * g.nbq + i) * 64 + 32 * qb + l32;
-    lse2[qb] = lse_c[ci] * kLog2e;
-    dl[qb] = delta_c[ci];
+    const float2 ld = ld_c[((size_t)bh * g.nbq + i) * 64 + 32 * qb + l32];
+    lse2[qb] = ld.x * kLog2e;
+    dl[qb] = ld.y;
   }
 
   f32x16 acc[DB][2];
 #pragma unroll
   for (int db = 0; db < DB; ++db) { zero16(acc[db][0]); zero16(acc[db][1]); }
+  const int trb = tr_lane_base(lane);
 
-  const int32_t* irow = idx + ((size_t)bh * g.nbq + i) * k_sel;
-  const size_t bh_bytes = (size_t)g.nbk * cube_bytes;
-  const size_t bh_elems = (size_t)g.nbk * 64 * D;
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(k_row + bh * bh_elems, bh_bytes);
-  const __amdgpu_buffer_rsrc_t rkt = make_rsrc(k_trans + bh * bh_elems, bh_bytes);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(v_row + bh * bh_elems, bh_bytes);
-  const int vlane = lane * 16;
-  const int ntiles = 2 * k_sel;
-
-  bf16x8 kr[S], vr[S], kt[DB * 2];
-  {
-    const int off0 = irow[0] * cube_bytes;
-#pragma unroll
-    for (int s = 0; s < S; ++s) {
-      kr[s] = bld16(rk, vlane, off0 + s * 1024);
-      vr[s] = bld16(rv, vlane, off0 + s * 1024);
-    }
-#pragma unroll
-    for (int u = 0; u < DB * 2; ++u) kt[u] = bld16(rkt, vlane, off0 + u * 1024);
-  }
-
-  for (int t = 0; t < ntiles; ++t) {
-    asm volatile("" ::: "memory");
+  auto tile = [&](int t, lds_char* cur, lds_char* nxt) {
+    // next tile's K and V rows -> the other stage (its previous reads were consumed last tile);
+    // the last tile re-stages itself so every tile waits the same way
+    const int tn = t + 1 < ntiles ? t + 1 : t;
+    const int noff = irow[tn >> 1] * cube_bytes + (tn & 1) * half_bytes;
+    stage_half<D>(rk, noff, nxt, lane);
+    stage_half<D>(rv, noff, nxt + half_bytes, lane);
+    __builtin_amdgcn_s_waitcnt(0x0f70 | ((2 * S) & 0xf) | (((2 * S) >> 4) << 14));  // vmcnt(2S)
     f32x16 st[2], dpt[2];
     zero16(st[0]); zero16(st[1]); zero16(dpt[0]); zero16(dpt[1]);
+    bf16x8 ka[S];
+#pragma unroll
+    for (int s = 0; s < S; ++s) ka[s] = lds_row_frag(cur, lane, s);
 #pragma unroll
     for (int s = 0; s < S; ++s) {
-      const bf16x8 q0 = qs[(s * 2 + 0) * 64 + lane];
-      const bf16x8 q1 = qs[(s * 2 + 1) * 64 + lane];
-      st[0] = mfma32(kr[s], q0, st[0]);
-      st[1] = mfma32(kr[s], q1, st[1]);
+      st[0] = mfma32(ka[s], qreg[0][s], st[0]);
+      st[1] = mfma32(ka[s], qreg[1][s], st[1]);
     }
 #pragma unroll
-    for (int s = 0; s < S; ++s) {
-      const bf16x8 d0 = dos[(s * 2 + 0) * 64 + lane];
-      const bf16x8 d1 = dos[(s * 2 + 1) * 64 + lane];
-      dpt[0] = mfma32(vr[s], d0, dpt[0]);
-      dpt[1] = mfma32(vr[s], d1, dpt[1]);
-    }
-    const int tn = t + 1 < ntiles ? t + 1 : t;
-    const int noff = irow[tn >> 1] * cube_bytes + (tn & 1) * (32 * D * 2);
+    for (int s = 0; s < S; ++s) ka[s] = lds_row_frag(cur + half_bytes, lane, s);
 #pragma unroll
     for (int s = 0; s < S; ++s) {
-      kr[s] = bld16(rk, vlane, noff + s * 1024);
-      vr[s] = bld16(rv, vlane, noff + s * 1024);
+      dpt[0] = mfma32(ka[s], dreg[0][s], dpt[0]);
+      dpt[1] = mfma32(ka[s], dreg[1][s], dpt[1]);
     }
+    bf16x8 kt[DB * 2];
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) kt[db * 2 + s2] = lds_trans_frag<D>(cur, trb, db, s2);
     bf16x8 dsb[2][2];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb)
@@ -149,12 +208,16 @@ __global__ __launch_bounds__(64) void bwd_dq_mfma_kernel(
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) acc[db][qb] = mfma32(kt[db * 2 + s2], dsb[s2][qb], acc[db][qb]);
-#pragma unroll
-    for (int u = 0; u < DB * 2; ++u) kt[u] = bld16(rkt, vlane, noff + u * 1024);
+      for (int s2 = 0; s2 < 2; ++s2) {
+        acc[db][0] = mfma32(kt[db * 2 + s2], dsb[s2][0], acc[db][0]);
+        acc[db][1] = mfma32(kt[db * 2 + s2], dsb[s2][1], acc[db][1]);
+      }
+  };
+  for (int t = 0; t < ntiles; t += 2) {
+    tile(t, st0, st1);
+    if (t + 1 < ntiles) tile(t + 1, st1, st0);
   }
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the last re-staging has landed
 
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
@@ -173,21 +236,27 @@ __global__ __launch_bounds__(64) void bwd_dq_mfma_kernel(
 }
 
 // ---------------------------------------------------------------------------------------------
-// dK, dV: grid = B*Hh*cpx*8, one wave per key cube (cond_T == 0, so key cube j = noise cube j).
+// dK, dV (key-stationary over the CSR transpose): grid = B*Hh*cpx*8, one wave per key cube
+// (cond_T == 0, so key cube j = noise cube j).  K and V rows of the key cube are B operands held
+// in registers; per 32-query half of each query cube that selected j, the Q and dO rows are staged
+// straight into LDS (double buffered), S = Q K^T and dP = dO V^T read them as A operands, and
+// P, dS built in place in the accumulators are the B operands of dV^T += dO^T P and
+// dK^T += Q^T dS, whose A operands are read transposed from the same staged rows.
 // ---------------------------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(64) void bwd_dkdv_mfma_kernel(
-    Geom g, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
-    const bf16_t* __restrict__ q_row, const bf16_t* __restrict__ q_trans,
-    const bf16_t* __restrict__ do_row, const bf16_t* __restrict__ do_trans,
-    const float* __restrict__ lse_c, const float* __restrict__ delta_c,
-    const int32_t* __restrict__ csr_off, const int32_t* __restrict__ csr_list, float scale,
-    float c_log2, int cpx, float* __restrict__ dk, float* __restrict__ dv) {
+    Geom g, const bf16_t* __restrict__ k_row, const bf16_t* __restrict__ v_row,
+    const bf16_t* __restrict__ q_row, const bf16_t* __restrict__ do_row,
+    const float2* __restrict__ ld_c, const int32_t* __restrict__ csr_off,
+    const int32_t* __restrict__ csr_list, float scale, float c_log2, int cpx,
+    float* __restrict__ dk, float* __restrict__ dv) {
   constexpr int S = D / 16;
   constexpr int DB = D / 32;
   constexpr int cube_bytes = 64 * D * 2;
-  __shared__ bf16x8 ks[2 * S * 64];
-  __shared__ bf16x8 vs[2 * S * 64];
+  constexpr int half_bytes = 32 * D * 2;
+  constexpr int stage_bytes = 2 * half_bytes + 256;  // Q rows | dO rows | 32 (LSE, Delta) pairs
+  __shared__ __attribute__((aligned(16))) char stage0[stage_bytes];
+  __shared__ __attribute__((aligned(16))) char stage1[stage_bytes];
 
   const int L = blockIdx.x;
   const int xcd = L & 7;
@@ -200,109 +269,101 @@ __global__ __launch_bounds__(64) void bwd_dkdv_mfma_kernel(
   const int l32 = lane & 31;
   const int hh = lane >> 5;
 
-  // K, V as B operands: lane = key, 8 consecutive d (same d split as the ROW layout).
+  const int32_t* offs = csr_off + (size_t)bh * (g.nbk + 1);
+  const int beg = offs[j], end = offs[j + 1];
+  const int nsteps = 2 * (end - beg);
+  const size_t bh_bytes = (size_t)g.nbq * cube_bytes;
+  const size_t bh_elems = (size_t)g.nbq * 64 * D;
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(q_row + bh * bh_elems, bh_bytes);
+  const __amdgpu_buffer_rsrc_t rd = make_rsrc(do_row + bh * bh_elems, bh_bytes);
+  const __amdgpu_buffer_rsrc_t rl =
+      make_rsrc(ld_c + (size_t)bh * g.nbq * 64, (size_t)g.nbq * 64 * sizeof(float2));
+  lds_char* st0 = (lds_char*)stage0;
+  lds_char* st1 = (lds_char*)stage1;
+  // one 32-query half of query cube i: Q rows, dO rows and the (LSE, Delta) pairs -> a stage
+  auto stage_step = [&](int i, int qb, lds_char* dst) {
+    stage_half<D>(rq, i * cube_bytes + qb * half_bytes, dst, lane);
+    stage_half<D>(rd, i * cube_bytes + qb * half_bytes, dst + half_bytes, lane);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rl, (__attribute__((address_space(3))) void*)(dst + 2 * half_bytes), 4, lane * 4,
+        (i * 64 + 32 * qb) * (int)sizeof(float2), 0, 0);
+  };
+  if (nsteps > 0) stage_step(csr_list[beg], 0, st0);
+
+  // K and V rows of this key cube as B operands (lane = key, 8 consecutive d).
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(k_row + bh * bh_elems, bh_bytes);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(v_row + bh * bh_elems, bh_bytes);
+  bf16x8 kreg[2][S], vreg[2][S];
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-    const int tk = cube_token(g, j, 32 * kb + l32);
-    const size_t off = bnhd_offset(g, g.Nq, b, tk, h) + hh * (D / 2);
+  for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
     for (int s = 0; s < S; ++s) {
-      ks[(kb * S + s) * 64 + lane] = ld16g(k + off + 8 * s);
-      vs[(kb * S + s) * 64 + lane] = ld16g(v + off + 8 * s);
+      kreg[kb][s] = bld16(rk, lane * 16, j * cube_bytes + (kb * S + s) * 1024);
+      vreg[kb][s] = bld16(rv, lane * 16, j * cube_bytes + (kb * S + s) * 1024);
     }
-  }
 
   f32x16 acck[DB][2], accv[DB][2];
 #pragma unroll
   for (int db = 0; db < DB; ++db)
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) { zero16(acck[db][kb]); zero16(accv[db][kb]); }
+  const int trb = tr_lane_base(lane);
 
-  const int32_t* offs = csr_off + (size_t)bh * (g.nbk + 1);
-  const int beg = offs[j], end = offs[j + 1];
-  const size_t bh_bytes = (size_t)g.nbq * cube_bytes;
-  const size_t bh_elems = (size_t)g.nbq * 64 * D;
-  const __amdgpu_buffer_rsrc_t rq = make_rsrc(q_row + bh * bh_elems, bh_bytes);
-  const __amdgpu_buffer_rsrc_t rqt = make_rsrc(q_trans + bh * bh_elems, bh_bytes);
-  const __amdgpu_buffer_rsrc_t rd = make_rsrc(do_row + bh * bh_elems, bh_bytes);
-  const __amdgpu_buffer_rsrc_t rdt = make_rsrc(do_trans + bh * bh_elems, bh_bytes);
-  const int vlane = lane * 16;
-  const float* lse_bh = lse_c + (size_t)bh * g.nbq * 64;
-  const float* dl_bh = delta_c + (size_t)bh * g.nbq * 64;
-  const int nsteps = 2 * (end - beg);
-
-  bf16x8 qr[S], dr[S];
-  if (nsteps > 0) {
-    const int off0 = csr_list[beg] * cube_bytes;
-#pragma unroll
-    for (int s = 0; s < S; ++s) {
-      qr[s] = bld16(rq, vlane, off0 + s * 1024);
-      dr[s] = bld16(rd, vlane, off0 + s * 1024);
-    }
-  }
-
-  for (int t = 0; t < nsteps; ++t) {
-    asm volatile("" ::: "memory");
-    const int i = csr_list[beg + (t >> 1)];
-    const int qb = t & 1;
-    const int coff = i * cube_bytes + qb * (32 * D * 2);
-    f32x16 st[2], dp[2];
-    zero16(st[0]); zero16(st[1]); zero16(dp[0]); zero16(dp[1]);
-#pragma unroll
-    for (int s = 0; s < S; ++s) {
-      st[0] = mfma32(qr[s], ks[(0 * S + s) * 64 + lane], st[0]);
-      st[1] = mfma32(qr[s], ks[(1 * S + s) * 64 + lane], st[1]);
-    }
-#pragma unroll
-    for (int s = 0; s < S; ++s) {
-      dp[0] = mfma32(dr[s], vs[(0 * S + s) * 64 + lane], dp[0]);
-      dp[1] = mfma32(dr[s], vs[(1 * S + s) * 64 + lane], dp[1]);
-    }
-    // transposed operands of this step, into registers the row operands no longer need
-    bf16x8 qt[DB * 2], dt[DB * 2];
-#pragma unroll
-    for (int u = 0; u < DB * 2; ++u) {
-      qt[u] = bld16(rqt, vlane, coff + u * 1024);
-      dt[u] = bld16(rdt, vlane, coff + u * 1024);
-    }
-    // P and dS for the 16 query rows this lane holds (rows 8*r4 + 4*hh + e4 of the 32-row half)
+  auto step = [&](int t, lds_char* cur, lds_char* nxt) {
+    const int tn = t + 1 < nsteps ? t + 1 : t;
+    stage_step(csr_list[beg + (tn >> 1)], tn & 1, nxt);
+    __builtin_amdgcn_s_waitcnt(0x0f70 | ((2 * S + 1) & 0xf) | (((2 * S + 1) >> 4) << 14));
+    // P and dS, key half by key half (rows 8*r4 + 4*hh + e4 of the 32-query half per lane)
     bf16x8 pb[2][2], dsb[2][2];
-    const float* lp = lse_bh + (size_t)i * 64 + 32 * qb + 4 * hh;
-    const float* dlp = dl_bh + (size_t)i * 64 + 32 * qb + 4 * hh;
+    const __attribute__((address_space(3))) f32x4* ldp =
+        (const __attribute__((address_space(3))) f32x4*)(cur + 2 * half_bytes);
 #pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) {
-      const float4 a4 = *reinterpret_cast<const float4*>(lp + 8 * r4);
-      const float4 c4 = *reinterpret_cast<const float4*>(dlp + 8 * r4);
-      const float la[4] = {a4.x * kLog2e, a4.y * kLog2e, a4.z * kLog2e, a4.w * kLog2e};
-      const float da[4] = {c4.x, c4.y, c4.z, c4.w};
+    for (int kb = 0; kb < 2; ++kb) {
+      // re-read the staged rows for each key half instead of keeping 32 fragments live
+      asm volatile("" ::: "memory");
+      f32x16 st, dp;
+      zero16(st);
+      zero16(dp);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int s = 0; s < S; ++s) st = mfma32(lds_row_frag(cur, lane, s), kreg[kb][s], st);
+#pragma unroll
+      for (int s = 0; s < S; ++s)
+        dp = mfma32(lds_row_frag(cur + half_bytes, lane, s), vreg[kb][s], dp);
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        // pairs (lse, delta) of rows 8*r4 + 4*hh + 0..3
+        const f32x4 p01 = ldp[(8 * r4 + 4 * hh) / 2];
+        const f32x4 p23 = ldp[(8 * r4 + 4 * hh) / 2 + 1];
+        const float lv[4] = {p01[0], p01[2], p23[0], p23[2]};
+        const float dv4[4] = {p01[1], p01[3], p23[1], p23[3]};
 #pragma unroll
         for (int e4 = 0; e4 < 4; ++e4) {
           const int r = 4 * r4 + e4;
-          const float p = fast_exp2(fmaf(st[kb][r], c_log2, -la[e4]));
+          const float p = fast_exp2(fmaf(st[r], c_log2, -lv[e4] * kLog2e));
           pb[kb][r >> 3][r & 7] = (__bf16)p;
-          dsb[kb][r >> 3][r & 7] = (__bf16)(p * (dp[kb][r] - da[e4]));
+          dsb[kb][r >> 3][r & 7] = (__bf16)(p * (dp[r] - dv4[e4]));
         }
+      }
     }
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const bf16x8 dt = lds_trans_frag<D>(cur + half_bytes, trb, db, s2);
+        const bf16x8 qt = lds_trans_frag<D>(cur, trb, db, s2);
 #pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-          accv[db][kb] = mfma32(dt[db * 2 + s2], pb[kb][s2], accv[db][kb]);
-          acck[db][kb] = mfma32(qt[db * 2 + s2], dsb[kb][s2], acck[db][kb]);
+        for (int kb = 0; kb < 2; ++kb) {
+          accv[db][kb] = mfma32(dt, pb[kb][s2], accv[db][kb]);
+          acck[db][kb] = mfma32(qt, dsb[kb][s2], acck[db][kb]);
         }
-    // row operands of the next step
-    const int tn = t + 1 < nsteps ? t + 1 : t;
-    const int noff = csr_list[beg + (tn >> 1)] * cube_bytes + (tn & 1) * (32 * D * 2);
-#pragma unroll
-    for (int s = 0; s < S; ++s) {
-      qr[s] = bld16(rq, vlane, noff + s * 1024);
-      dr[s] = bld16(rd, vlane, noff + s * 1024);
-    }
+      }
+  };
+  for (int t = 0; t < nsteps; ++t) {
+    lds_char* cur = (t & 1) ? st1 : st0;
+    lds_char* nxt = (t & 1) ? st0 : st1;
+    step(t, cur, nxt);
   }
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the last re-staging has landed
 
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
@@ -324,41 +385,35 @@ __global__ __launch_bounds__(64) void bwd_dkdv_mfma_kernel(
   }
 }
 
-hipError_t launch_bwd_dq_mfma(const Geom& g, const void* q, const void* d_o,
-                              const bf16_t* k_row, const bf16_t* k_trans, const bf16_t* v_row,
-                              const float* lse_c, const float* delta_c, const int32_t* idx,
-                              int k_sel, float scale, float* dq, hipStream_t s) {
+hipError_t launch_bwd_dq_mfma(const Geom& g, const bf16_t* q_row, const bf16_t* do_row,
+                              const bf16_t* k_row, const bf16_t* v_row, const float2* ld_c,
+                              const int32_t* idx, int k_sel, float scale, float* dq,
+                              hipStream_t s) {
   const int cpx = (g.nbq + 7) / 8;
   dim3 grid((unsigned)(g.B * g.Hh * cpx * 8));
   const float c_log2 = scale * kLog2e;
   if (g.D == 64)
-    hipLaunchKernelGGL(bwd_dq_mfma_kernel<64>, grid, dim3(64), 0, s, g, (const bf16_t*)q,
-                       (const bf16_t*)d_o, k_row, k_trans, v_row, lse_c, delta_c, idx, k_sel,
-                       scale, c_log2, cpx, dq);
+    hipLaunchKernelGGL(bwd_dq_mfma_kernel<64>, grid, dim3(64), 0, s, g, q_row, do_row, k_row,
+                       v_row, ld_c, idx, k_sel, scale, c_log2, cpx, dq);
   else
-    hipLaunchKernelGGL(bwd_dq_mfma_kernel<128>, grid, dim3(64), 0, s, g, (const bf16_t*)q,
-                       (const bf16_t*)d_o, k_row, k_trans, v_row, lse_c, delta_c, idx, k_sel,
-                       scale, c_log2, cpx, dq);
+    hipLaunchKernelGGL(bwd_dq_mfma_kernel<128>, grid, dim3(64), 0, s, g, q_row, do_row, k_row,
+                       v_row, ld_c, idx, k_sel, scale, c_log2, cpx, dq);
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_dkdv_mfma(const Geom& g, const void* k, const void* v,
-                                const bf16_t* q_row, const bf16_t* q_trans,
-                                const bf16_t* do_row, const bf16_t* do_trans,
-                                const float* lse_c, const float* delta_c,
+hipError_t launch_bwd_dkdv_mfma(const Geom& g, const bf16_t* k_row, const bf16_t* v_row,
+                                const bf16_t* q_row, const bf16_t* do_row, const float2* ld_c,
                                 const int32_t* csr_off, const int32_t* csr_list, float scale,
                                 float* dk, float* dv, hipStream_t s) {
   const int cpx = (g.nbq + 7) / 8;
   dim3 grid((unsigned)(g.B * g.Hh * cpx * 8));
   const float c_log2 = scale * kLog2e;
   if (g.D == 64)
-    hipLaunchKernelGGL(bwd_dkdv_mfma_kernel<64>, grid, dim3(64), 0, s, g, (const bf16_t*)k,
-                       (const bf16_t*)v, q_row, q_trans, do_row, do_trans, lse_c, delta_c,
-                       csr_off, csr_list, scale, c_log2, cpx, dk, dv);
+    hipLaunchKernelGGL(bwd_dkdv_mfma_kernel<64>, grid, dim3(64), 0, s, g, k_row, v_row, q_row,
+                       do_row, ld_c, csr_off, csr_list, scale, c_log2, cpx, dk, dv);
   else
-    hipLaunchKernelGGL(bwd_dkdv_mfma_kernel<128>, grid, dim3(64), 0, s, g, (const bf16_t*)k,
-                       (const bf16_t*)v, q_row, q_trans, do_row, do_trans, lse_c, delta_c,
-                       csr_off, csr_list, scale, c_log2, cpx, dk, dv);
+    hipLaunchKernelGGL(bwd_dkdv_mfma_kernel<128>, grid, dim3(64), 0, s, g, k_row, v_row, q_row,
+                       do_row, ld_c, csr_off, csr_list, scale, c_log2, cpx, dk, dv);
   return hipGetLastError();
 }
 

@@ -21,7 +21,8 @@ __global__ __launch_bounds__(64) void delta_kernel(Geom g, const T* __restrict__
                                                    const T* __restrict__ d_o,
                                                    const float* __restrict__ lse,
                                                    float* __restrict__ delta_c,
-                                                   float* __restrict__ lse_c) {
+                                                   float* __restrict__ lse_c,
+                                                   float2* __restrict__ ld_c) {
   constexpr int V = 16 / sizeof(T);
   const int i = blockIdx.x;
   const int bh = blockIdx.y;
@@ -48,21 +49,24 @@ __global__ __launch_bounds__(64) void delta_kernel(Geom g, const T* __restrict__
     for (int off = lpr >> 1; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
     if (s < g.c && sub == 0) {
       const size_t dst = ((size_t)bh * g.nbq + i) * g.c + s;
+      const float lv = lse[(size_t)bh * g.Nq + tok];
       delta_c[dst] = acc;
-      lse_c[dst] = lse[(size_t)bh * g.Nq + tok];
+      lse_c[dst] = lv;
+      if (ld_c) ld_c[dst] = make_float2(lv, acc);
     }
   }
 }
 
 hipError_t launch_delta(const Geom& g, bool bf16, const void* o, const void* d_o,
-                        const float* lse, float* delta_c, float* lse_c, hipStream_t s) {
+                        const float* lse, float* delta_c, float* lse_c, float2* ld_c,
+                        hipStream_t s) {
   dim3 grid(g.nbq, g.B * g.Hh);
   if (bf16)
     hipLaunchKernelGGL(delta_kernel<bf16_t>, grid, dim3(64), 0, s, g, (const bf16_t*)o,
-                       (const bf16_t*)d_o, lse, delta_c, lse_c);
+                       (const bf16_t*)d_o, lse, delta_c, lse_c, ld_c);
   else
     hipLaunchKernelGGL(delta_kernel<float>, grid, dim3(64), 0, s, g, (const float*)o,
-                       (const float*)d_o, lse, delta_c, lse_c);
+                       (const float*)d_o, lse, delta_c, lse_c, ld_c);
   return hipGetLastError();
 }
 
