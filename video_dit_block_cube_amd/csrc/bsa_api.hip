@@ -131,9 +131,9 @@ BwdWs bwd_layout(const Geom& g, bool mfma, int k_sel) {
 
 // Key-range split count of the MFMA forward: BSA_FWD_SPLITS overrides the size-based choice
 // (tuning aid; 1 disables the split).
-int fwd_splits(const Geom& g) {
+int fwd_splits(const Geom& g, int k_sel) {
   const char* env = std::getenv("BSA_FWD_SPLITS");
-  return fwd_split_ranges(g, env ? std::atoi(env) : -1);
+  return fwd_split_ranges(g, k_sel, env ? std::atoi(env) : -1);
 }
 
 // The query-only view of a problem (no condition segment): gathers of Q cover the noise cubes.
@@ -143,10 +143,10 @@ Geom noise_only(const Geom& g) {
 
 // Forward workspace (MFMA path): K rows + V^T over all nbk key cubes, Q rows over the nbq query
 // cubes, then the key-range partials.
-size_t fwd_ws(const Geom& g, bool mfma) {
+size_t fwd_ws(const Geom& g, bool mfma, int k_sel) {
   if (!mfma) return 0;
   return 2 * align_up(gather_bytes(g, true)) + align_up(gather_bytes(noise_only(g), true)) +
-         align_up(fwd_split_bytes(g, fwd_splits(g)));
+         align_up(fwd_split_bytes(g, fwd_splits(g, k_sel)));
 }
 
 template <typename F>
@@ -218,7 +218,7 @@ bsa_status_t bsa_sparse_attn_fwd(const bsa_problem_t* p, bsa_dtype_t dtype, cons
       return fail(BSA_ERR_INVALID_ARG, "k_cache / v_cache given but cond_T == 0");
     if (!std::isfinite(softmax_scale)) return fail(BSA_ERR_INVALID_ARG, "softmax_scale not finite");
     const bool mfma = use_mfma(g, dtype);
-    const size_t need = fwd_ws(g, mfma);
+    const size_t need = fwd_ws(g, mfma, k_sel);
     if (need > 0 && (!ws || ws_bytes < need))
       return fail(BSA_ERR_WORKSPACE, "workspace smaller than bsa_workspace_bytes()");
     Stages stages(stream);
@@ -240,7 +240,7 @@ bsa_status_t bsa_sparse_attn_fwd(const bsa_problem_t* p, bsa_dtype_t dtype, cons
                       "gather Q");
       if (st != BSA_OK) return st;
       stages.done("gather_qkv");
-      const int ns = fwd_splits(g);
+      const int ns = fwd_splits(g, k_sel);
       st = hip_status(launch_fwd_mfma(g, qrow, krow, vtr, idx, k_sel, softmax_scale, o, lse, ns,
                                       split_ws, stream),
                       "attention forward launch");
@@ -340,7 +340,7 @@ size_t bsa_workspace_bytes(const bsa_problem_t* p, bsa_dtype_t dtype, int32_t k_
       check_ksel(g, k_sel) != BSA_OK)
     return (size_t)-1;
   const bool mfma = use_mfma(g, dtype);
-  return bwd ? bwd_layout(g, mfma, k_sel).total : fwd_ws(g, mfma);
+  return bwd ? bwd_layout(g, mfma, k_sel).total : fwd_ws(g, mfma, k_sel);
 }
 
 const char* bsa_status_string(bsa_status_t s) {

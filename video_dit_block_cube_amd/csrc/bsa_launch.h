@@ -53,7 +53,7 @@ hipError_t launch_gather(const Geom& g, const void* x, const void* x_cache, int 
 // layout over the nbq query cubes ([B, Hh, nbq, 64*D]).  ns <= 1 runs one pass per
 // query cube; ns > 1 splits the key cube ids into ns ranges (one XCD's L2 per range) and merges
 // the partials, which need fwd_split_bytes(g, ns) bytes of split_ws.
-int fwd_split_ranges(const Geom& g, int requested);
+int fwd_split_ranges(const Geom& g, int k_sel, int requested);
 size_t fwd_split_bytes(const Geom& g, int ns);
 hipError_t launch_fwd_mfma(const Geom& g, const bf16_t* q_row, const bf16_t* k_row,
                            const bf16_t* v_trans, const int32_t* idx, int k_sel, float scale,

@@ -88,22 +88,25 @@ __device__ __forceinline__ bf16x8 pack8(const f32x16& a, int base) {
 }  // namespace
 
 // Online-softmax attention of one 64-token query cube over the 32-key half cubes
-// [t_begin, t_end) of its (ascending) selection row.  Accumulates O^T (unnormalised), the running
-// base-2 max and this lane's partial row sums.
+// [t_begin, t_end) of its (ascending) selection row, where row position p stands for entry
+// p + (p >= p_split ? p_skip : 0) (two disjoint spans walked as one; p_skip = 0 for one span).
+// Accumulates O^T (unnormalised), the running base-2 max and this lane's partial row sums.
 template <int D, bool EARLY_K>
 __device__ __forceinline__ void attend_span(const bf16x8* __restrict__ qs,
                                             __amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv,
                                             const int32_t* __restrict__ irow, int t_begin,
-                                            int t_end, float c_log2, int lane,
-                                            f32x16 (&acc)[D / 32][2], float (&m_run)[2],
-                                            float (&l_part)[2]) {
+                                            int t_end, int p_split, int p_skip, float c_log2,
+                                            int lane, f32x16 (&acc)[D / 32][2],
+                                            float (&m_run)[2], float (&l_part)[2]) {
   constexpr int S = D / 16;
   constexpr int DB = D / 32;
   constexpr int cube_bytes = 64 * D * 2;
   const int vlane = lane * 16;
   bf16x8 kr[S], vr[DB * 2];
   {
-    const int off0 = irow[t_begin >> 1] * cube_bytes + (t_begin & 1) * (32 * D * 2);
+    const int p0 = t_begin >> 1;
+    const int off0 =
+        irow[p0 + (p0 >= p_split ? p_skip : 0)] * cube_bytes + (t_begin & 1) * (32 * D * 2);
 #pragma unroll
     for (int s = 0; s < S; ++s) kr[s] = bld16(rk, vlane, off0 + s * 1024);
 #pragma unroll
@@ -127,7 +130,8 @@ __device__ __forceinline__ void attend_span(const bf16x8* __restrict__ qs,
       st[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr[s], q1, st[1], 0, 0, 0);
     }
     const int tn = t + 1 < t_end ? t + 1 : t;
-    const int noff = irow[tn >> 1] * cube_bytes + (tn & 1) * (32 * D * 2);
+    const int pn = tn >> 1;
+    const int noff = irow[pn + (pn >= p_split ? p_skip : 0)] * cube_bytes + (tn & 1) * (32 * D * 2);
     if constexpr (EARLY_K) {
       // ---- request next tile's K now (longer lead, more live registers) ----
 #pragma unroll
@@ -230,7 +234,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   zero_acc<D>(acc);
   float m_run[2] = {-INFINITY, -INFINITY};
   float l_part[2] = {0.f, 0.f};
-  attend_span<D, EARLY_K>(qs, rk, rv, irow, 0, 2 * k_sel, c_log2, lane, acc, m_run, l_part);
+  attend_span<D, EARLY_K>(qs, rk, rv, irow, 0, 2 * k_sel, k_sel, 0, c_log2, lane, acc, m_run,
+                          l_part);
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     const float l = l_part[qb] + __shfl_xor(l_part[qb], 32, 64);
@@ -252,16 +257,18 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   }
 }
 
-// Split over key ranges: key cube ids are cut into NS contiguous ranges of `rc` cubes; work item
-// (range s, b, h, query cube i) attends only the selected cubes of range s and writes a normalised
-// partial O (bf16, [64][D] row-major) plus its base-2 max and row sum.  Range s runs on XCD s%8,
-// whose L2 then only ever holds that range of the head's K/V; the XCD takes its ranges one after
-// the other (s = xcd, xcd + 8, ...), heads in order within each.
+// Split over key ranges: range s holds the s-th of NS contiguous runs of the condition cube ids
+// (`rcc` cubes each) and the s-th of NS runs of the noise cube ids (`rcn` each), so every range
+// carries the same share of the always-selected condition cubes.  Work item (range s, b, h, query
+// cube i) attends only the selected cubes of range s and writes a normalised partial O (bf16,
+// [64][D] row-major) plus its base-2 max and row sum.  Range s runs on XCD s%8, whose L2 then
+// only ever holds that range of the head's K/V; the XCD takes its ranges one after the other
+// (s = xcd, xcd + 8, ...), heads in order within each.
 template <int D, bool EARLY_K>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_split_kernel(
     Geom g, const bf16_t* __restrict__ q_row, const bf16_t* __restrict__ krow,
     const bf16_t* __restrict__ vtr, const int32_t* __restrict__ idx, int k_sel, float c_log2,
-    int ns, int rc, bf16_t* __restrict__ o_part, float2* __restrict__ ml_part) {
+    int ns, int rcc, int rcn, bf16_t* __restrict__ o_part, float2* __restrict__ ml_part) {
   constexpr int DB = D / 32;
   constexpr int cube_bytes = 64 * D * 2;
   __shared__ bf16x8 qs[(D / 16) * 2 * 64];
@@ -279,11 +286,14 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   const int lane = threadIdx.x;
   const int l32 = lane & 31, hh = lane >> 5;
   const int32_t* irow = idx + ((size_t)bh * g.nbq + i) * k_sel;
-  int lo, hi;
-  row_span(irow, k_sel, sr * rc, (sr + 1) * rc, lane, lo, hi);
+  int lo1, hi1, lo2, hi2;  // selected condition cubes of the range, then its noise cubes
+  row_span(irow, k_sel, sr * rcc, min((sr + 1) * rcc, g.nbc), lane, lo1, hi1);
+  row_span(irow, k_sel, g.nbc + sr * rcn, g.nbc + (sr + 1) * rcn, lane, lo2, hi2);
+  if (hi1 < lo1) hi1 = lo1;  // empty condition run (sr * rcc >= nbc)
+  const int n_sel = (hi1 - lo1) + (hi2 - lo2);
   const size_t item = ((size_t)sr * g.B * g.Hh + bh) * g.nbq + i;
   float2* ml = ml_part + item * 64;
-  if (lo == hi) {
+  if (n_sel == 0) {
     if (hh == 0) {
       ml[l32] = make_float2(-INFINITY, 0.f);
       ml[32 + l32] = make_float2(-INFINITY, 0.f);
@@ -300,7 +310,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   zero_acc<D>(acc);
   float m_run[2] = {-INFINITY, -INFINITY};
   float l_part[2] = {0.f, 0.f};
-  attend_span<D, EARLY_K>(qs, rk, rv, irow, 2 * lo, 2 * hi, c_log2, lane, acc, m_run, l_part);
+  attend_span<D, EARLY_K>(qs, rk, rv, irow, 2 * lo1, 2 * (lo1 + n_sel), hi1, lo2 - hi1, c_log2,
+                          lane, acc, m_run, l_part);
   bf16_t* op = o_part + item * (64 * D);
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
@@ -385,11 +396,15 @@ size_t fwd_split_bytes(const Geom& g, int ns) {
   return items * 64 * g.D * sizeof(bf16_t) + items * 64 * sizeof(float2) + 256;
 }
 
-int fwd_split_ranges(const Geom& g, int requested) {
+int fwd_split_ranges(const Geom& g, int k_sel, int requested) {
   if (requested >= 0) return requested <= 1 ? 1 : requested;
-  // Split when one head's gathered K/V (32 KB per cube) is far larger than one XCD's 4 MB L2.
-  const double head_kv = (double)g.nbk * 64 * g.D * 2 * 2;
-  return head_kv > 8.0 * (1 << 20) ? 8 : 1;
+  // Split when the noise cubes a query cube selects out of a head's noise K/V (32 KB per cube)
+  // are most of its row and that K/V is far larger than one XCD's 4 MB L2.  When the forced
+  // condition cubes dominate, every query cube streams them in the same ascending order and
+  // the L2 already reuses them; the partials and their merge would only add work.
+  const double head_kv = (double)g.nbq * 64 * g.D * 2 * 2;
+  const bool mostly_noise = 2 * (k_sel - g.nbc) >= k_sel;
+  return (head_kv > 8.0 * (1 << 20) && mostly_noise) ? 8 : 1;
 }
 
 template <int D, bool EK>
@@ -404,14 +419,15 @@ static hipError_t launch_fwd_t(const Geom& g, const bf16_t* q_row, const bf16_t*
                        k_row, v_trans, idx, k_sel, c_log2, cpx, (bf16_t*)o, lse);
     return hipGetLastError();
   }
-  const int rc = (g.nbk + ns - 1) / ns;
+  const int rcc = (g.nbc + ns - 1) / ns;
+  const int rcn = (g.nbq + ns - 1) / ns;
   const size_t items = (size_t)ns * g.B * g.Hh * g.nbq;
   bf16_t* o_part = static_cast<bf16_t*>(split_ws);
   float2* ml_part = reinterpret_cast<float2*>(o_part + items * 64 * g.D);
   const int passes = (ns + 7) / 8;
   dim3 grid((unsigned)(8 * passes * g.B * g.Hh * g.nbq));
   hipLaunchKernelGGL((fwd_split_kernel<D, EK>), grid, dim3(64), 0, s, g, q_row,
-                     k_row, v_trans, idx, k_sel, c_log2, ns, rc, o_part, ml_part);
+                     k_row, v_trans, idx, k_sel, c_log2, ns, rcc, rcn, o_part, ml_part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   dim3 mgrid(g.nbq, g.B * g.Hh);
