@@ -108,6 +108,8 @@ def main() -> int:
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-continuation", action="store_true",
                     help="skip the continuation-mode forward measurement")
+    ap.add_argument("--no-dense", action="store_true",
+                    help="skip the dense-attention (r = all) forward comparison")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -231,6 +233,8 @@ def main() -> int:
 
     if not args.no_continuation:
         out["continuation_fwd"] = bench_continuation(bsa, synth, orc, torch, dev, args)
+    if not args.no_dense:
+        out["dense_vs_bsa_fwd"] = bench_dense(bsa, synth, torch, dev, t)
 
     if args.calib_copy_mib:
         n = args.calib_copy_mib * (1 << 20) // 4
@@ -290,6 +294,59 @@ def bench_continuation(bsa, synth, orc, torch, dev, args):
             "k_sel": ks, "tflop": round(f / 1e12, 3), "gather_ms": round(avg.get("gather_qkv", 0), 3),
             "attn_ms": round(attn, 3), "attn_tflops": round(f / (attn * 1e-3) / 1e12, 1),
             "frac_peak": round(f / (attn * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+
+
+def _time_fwd(bsa, torch, p, t, r, reps=3):
+    """Pool, select (r) and then the forward alone, timed per stage with HIP events."""
+    import numpy as np
+    ks = bsa.bsa_num_selected(p, r)
+    scale = 1.0 / math.sqrt(p.head_dim)
+    qm = bsa.bsa_block_pool(p, t["q"])
+    km = bsa.bsa_block_pool(p, t["k"])
+    idx, _ = bsa.bsa_select_topr(p, qm, km, r, with_mask=False)
+    ws = torch.empty(bsa.bsa_workspace_bytes(p, torch.bfloat16, ks, False), dtype=torch.uint8,
+                     device=t["q"].device)
+    o = torch.empty_like(t["q"])
+    lse = torch.empty((p.batch, p.heads, p.Nq), dtype=torch.float32, device=t["q"].device)
+    bsa.bsa_sparse_attn_fwd(p, t["q"], t["k"], t["v"], idx, ks, scale, o=o, lse=lse, workspace=ws)
+    torch.cuda.synchronize()
+    evs = [bsa.StageEvents(4) for _ in range(reps)]
+    for ev in evs:
+        with ev:
+            bsa.bsa_sparse_attn_fwd(p, t["q"], t["k"], t["v"], idx, ks, scale, o=o, lse=lse,
+                                    workspace=ws)
+    torch.cuda.synchronize()
+    tot = [sum(ms for _, ms in ev.elapsed_all()) for ev in evs]
+    del ws, idx
+    return ks, float(np.median(tot))
+
+
+def bench_dense(bsa, synth, torch, dev, t720):
+    """Dense 3D attention (r = all key cubes, the same kernels) against BSA at the 480p- and
+    720p-class grids: forward ms (gathers + attention) and the BSA speedup."""
+    res = {}
+    for number in (2, 3):
+        w = synth.workload(number)
+        if number == 3:
+            t = t720
+        else:
+            log(f"drawing inputs for {w.name}")
+            x = synth.make_inputs(w)
+            t = {k: torch.from_numpy(v).to(dev).to(torch.bfloat16) for k, v in x.items()
+                 if k in ("q", "k", "v")}
+            del x
+        p = bsa.Problem(**w.shape_dict)
+        ks_b, ms_b = _time_fwd(bsa, torch, p, t, w.r)
+        ks_d, ms_d = _time_fwd(bsa, torch, p, t, p.nbq - 1)
+        dense_f = 4.0 * p.batch * p.heads * p.Nq * p.Nq * p.head_dim
+        tag = "480p" if number == 2 else "720p"
+        res[tag] = {"grid": f"{p.T}x{p.H}x{p.W}", "bsa_k_sel": ks_b, "bsa_fwd_ms": round(ms_b, 3),
+                    "dense_fwd_ms": round(ms_d, 3), "dense_tflop": round(dense_f / 1e12, 2),
+                    "dense_tflops": round(dense_f / (ms_d * 1e-3) / 1e12, 1),
+                    "dense_frac_peak": round(dense_f / (ms_d * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                    "bsa_speedup": round(ms_d / ms_b, 2)}
+        log(f"dense vs BSA at {tag}: {ms_d:.2f} ms vs {ms_b:.2f} ms")
+    return res
 
 
 if __name__ == "__main__":

@@ -116,6 +116,41 @@ def test_fwd_key_range_split(splits, early, monkeypatch):
         assert_close(lse.cpu().numpy(), LSE, "bf16", "LSE", max_abs=2e-3, rel=1e-5)
 
 
+@pytest.mark.parametrize("splits", ["1", "8"])
+def test_fwd_dense_selection(splits, monkeypatch):
+    """r = all key cubes through the library's own pool and select, so the forward is dense
+    3D attention; checked against the oracle and a plain masked-free softmax in fp64."""
+    monkeypatch.setenv("BSA_FWD_SPLITS", splits)
+    bsa.bsa_set_kernel_path(AUTO)
+    w, x = cached_inputs(2, (("heads", 2), ("T", 8), ("H", 16), ("W", 32)))
+    print_case(f"fwd dense splits={splits} {w.name}")
+    p = bsa.Problem(**w.shape_dict)
+    op = orc.Problem(**w.shape_dict)
+    t = {k: to_dev(v, w.dtype) for k, v in x.items()}
+    r = op.nbq - 1
+    ks = orc.num_selected(op, r)
+    assert ks == op.nbq
+    qm = bsa.bsa_block_pool(p, t["q"])
+    km = bsa.bsa_block_pool(p, t["k"])
+    idx_d, _ = bsa.bsa_select_topr(p, qm, km, r, with_mask=False)
+    idx = idx_d.cpu().numpy()
+    assert (idx == np.arange(op.nbq, dtype=np.int32)).all()
+    scale = scale_of(op)
+    o, lse = bsa.bsa_sparse_attn_fwd(p, t["q"], t["k"], t["v"], idx_d, ks, scale)
+    O, LSE = orc.sparse_attn_fwd(x["q"], x["k"], x["v"], None, None, idx, op, scale)
+    assert_close(o.float().cpu().numpy(), O, "bf16", "O")
+    assert_close(lse.cpu().numpy(), LSE, "bf16", "LSE", max_abs=2e-3, rel=1e-5)
+    # head 1 against textbook dense attention (token order is irrelevant to dense softmax)
+    q = x["q"][0, :, 1].astype(np.float64)
+    k = x["k"][0, :, 1].astype(np.float64)
+    v = x["v"][0, :, 1].astype(np.float64)
+    s_ = scale * q[:512] @ k.T
+    m = s_.max(axis=1, keepdims=True)
+    e = np.exp(s_ - m)
+    ref = (e @ v) / e.sum(axis=1, keepdims=True)
+    assert_close(o[0, :512, 1].float().cpu().numpy(), ref, "bf16", "O dense")
+
+
 def _gpu_selection(w, t, p):
     qm = bsa.bsa_block_pool(p, t["q"])
     km = bsa.bsa_block_pool(p, t["k"])
