@@ -7,16 +7,18 @@
 //   dK_j += scale*dS^T Q_i.
 //
 // MI355X design: two kernels, each owning its output in registers so no fp32 atomics are needed.
-//  * dQ (query-stationary, one wave = one 64-token query cube): Q^T and dO^T operand fragments in
-//    LDS; per 32-key half cube, S^T = K Q^T and dP^T = V dO^T on MFMA (K, V from the ROW gather
-//    layout), then dS^T in place in the accumulator registers, converted to bf16, is the B
-//    operand of dQ^T += K^T dS^T (K^T from the TRANS gather layout).
-//  * dK/dV (key-stationary over the CSR transpose, one wave = one 64-token key cube): K and V in
-//    LDS as B operands; per 32-query half of each query cube that selected this key cube,
-//    S = Q K^T and dP = dO V^T (Q, dO from ROW layouts), then P and dS converted in place are
-//    the B operands of dV^T += dO^T P and dK^T += Q^T dS (dO^T, Q^T from TRANS layouts).
-//  Operands of the next step are requested as soon as the current ones are consumed; per-lane
-//  byte offsets stay constant and the wave-uniform tile offset rides in an SGPR (buffer loads).
+// Every operand comes from the ROW gather layout (lane = token, 8 consecutive d per 16 bytes);
+// the streamed operand's rows are staged straight into LDS with buffer_load ... lds and its
+// transposed uses are read back with ds_read_b64_tr_b16, so each tile crosses the fabric once.
+//  * dQ (query-stationary, one wave = one 64-token query cube): Q and dO rows in registers; per
+//    32-key half cube, K and V rows staged in LDS; S^T = K Q^T and dP^T = V dO^T on MFMA, dS^T in
+//    place in the accumulators, converted to bf16, is the B operand of dQ^T += K^T dS^T.
+//  * dK/dV (key-stationary over the CSR transpose, one wave = one 64-token key cube): K and V
+//    rows in registers; per 32-query half of each query cube that selected this key cube, Q and
+//    dO rows staged in LDS; S = Q K^T and dP = dO V^T, then P and dS converted in place are the
+//    B operands of dV^T += dO^T P and dK^T += Q^T dS.
+//  The next tile is requested as soon as the current one is staged; per-lane byte offsets stay
+//  constant and the wave-uniform tile offset rides in an SGPR (buffer loads).
 #include "bsa_launch.h"
 
 namespace bsa {
