@@ -108,6 +108,8 @@ def main() -> int:
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-continuation", action="store_true",
                     help="skip the continuation-mode forward measurement")
+    ap.add_argument("--no-prologue", action="store_true",
+                    help="skip the fused QK-norm + 3D RoPE prologue measurement")
     ap.add_argument("--no-dense", action="store_true",
                     help="skip the dense-attention (r = all) forward comparison")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -235,6 +237,8 @@ def main() -> int:
         out["continuation_fwd"] = bench_continuation(bsa, synth, orc, torch, dev, args)
     if not args.no_dense:
         out["dense_vs_bsa_fwd"] = bench_dense(bsa, synth, torch, dev, t)
+    if not args.no_prologue:
+        out["qk_prologue"] = bench_prologue(bsa, torch, dev, p)
 
     if args.calib_copy_mib:
         n = args.calib_copy_mib * (1 << 20) // 4
@@ -319,6 +323,43 @@ def _time_fwd(bsa, torch, p, t, r, reps=3):
     tot = [sum(ms for _, ms in ev.elapsed_all()) for ev in evs]
     del ws, idx
     return ks, float(np.median(tot))
+
+
+def bench_prologue(bsa, torch, dev, p, reps=5):
+    """QK RMS normalisation + 3D RoPE of one raw [B, Nq, Hh, D] bf16 tensor at the 720p-class
+    grid, fused with the cube means, against the same prologue followed by a separate pool."""
+    import numpy as np
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1234)
+    x = torch.randn((p.batch, p.Nq, p.heads, p.head_dim), generator=gen, device=dev,
+                    dtype=torch.float32).to(torch.bfloat16)
+    y = torch.empty_like(x)
+    m = torch.empty((p.batch, p.heads, p.nbq, p.head_dim), dtype=torch.float32, device=dev)
+
+    def timed(fn):
+        # both variants launch on torch's current stream, so stream events bracket them whole
+        fn()
+        torch.cuda.synchronize()
+        out = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            e1.synchronize()
+            out.append(e0.elapsed_time(e1))
+        return float(np.median(out))
+
+    fused = timed(lambda: bsa.bsa_qk_prologue(p, x, out=y, mean=m))
+    split = timed(lambda: (bsa.bsa_qk_prologue(p, x, out=y, with_mean=False),
+                           bsa.bsa_block_pool(p, y, m)))
+    nbytes = 2 * x.numel() * 2 + m.numel() * 4
+    return {"workload": f"raw bf16 [1, {p.Nq}, {p.heads}, {p.head_dim}] -> normalised, rotated "
+                        "tensor + fp32 cube means",
+            "fused_ms": round(fused, 4), "prologue_then_pool_ms": round(split, 4),
+            "algorithmic_bytes": nbytes,
+            "achieved_GBps": round(nbytes / (fused * 1e-3) / 1e9, 1),
+            "frac_hbm_peak": round(nbytes / (fused * 1e-3) / 1e9 / 8000.0, 4)}
 
 
 def bench_dense(bsa, synth, torch, dev, t720):

@@ -84,6 +84,29 @@ typedef struct {
 bsa_status_t bsa_block_pool(const bsa_problem_t* p, bsa_dtype_t dtype, const void* x,
                             float* x_mean, hipStream_t stream);
 
+/* Attention prologue fused with the cube pool: QK RMS normalisation (RMSNorm + QKNorm) and 3D
+ * rotary position embedding over time, height and width (youleyou page, section "三、模型架构";
+ * ai-news-5min-kr deep dive, layer table row for the positional encoding), then the per-cube
+ * means of the result, in one pass over x.  The pages give no formula; per (token, head):
+ *   y = x / sqrt(mean_d x^2 + eps) * gamma[d], then channel pairs (2i, 2i+1) of the time, height
+ *   and width blocks (contiguous, widths D - 4*floor(D/6), 2*floor(D/6), 2*floor(D/6)) rotated by
+ *   the angle pos_axis * rope_theta^(-2i / block width); pos = the token's (t, h, w) on the full
+ *   latent grid, condition frames first (noise frame f has t = cond_T + f).
+ *   segment  0: the noise segment, x [B, Nq, Hh, D]; 1: the condition segment (needs cond_T > 0),
+ *            x [B, cond_T*H*W, Hh, D]
+ *   x        device, dtype, read
+ *   gamma    device, [D] fp32 per-channel gain, or NULL for all ones
+ *   rope_theta  rotation base (10000 is the usual choice), finite and > 1
+ *   eps      finite and > 0 (1e-6 is the usual choice)
+ *   x_out    device, same shape and dtype as x, written (RNE to bf16); may equal x (in place)
+ *   x_mean   device, [B, Hh, nbq, D] fp32, written with the cube means of y before rounding
+ *            (segment 0 only; NULL skips it; must be NULL for segment 1)
+ * Errors: INVALID_ARG (null x / x_out, bad segment, theta, eps, x_mean with segment 1), SHAPE,
+ * UNSUPPORTED, HIP. */
+bsa_status_t bsa_qk_prologue(const bsa_problem_t* p, bsa_dtype_t dtype, int32_t segment,
+                             const void* x, const float* gamma, float rope_theta, float eps,
+                             void* x_out, float* x_mean, hipStream_t stream);
+
 /* Score every candidate key cube against each query cube and keep the top r (top-r key blocks,
  * youleyou page, section "块稀疏注意力（BSA）"; similarity-based choice, Data Science in Your Pocket
  * page, section "Sparse attention"; own block always kept, ai-news-5min-kr deep dive, same-table

@@ -117,3 +117,22 @@ def test_status_strings_and_path_switch(L):
     assert L.bsa_set_kernel_path(1) == OK
     assert L.bsa_set_kernel_path(0) == OK
     assert L.bsa_stage_name(-1) == b""
+
+
+def test_prologue_argument_errors(L):
+    f = L.bsa_qk_prologue
+    p = ctypes.byref(_p())
+    pc = ctypes.byref(_p(T=8, cond_T=4))
+    one = ctypes.c_float(10000.0)
+    e = ctypes.c_float(1e-6)
+    assert f(p, 1, 0, None, None, one, e, FAKE, FAKE, None) == INVALID        # null x
+    assert f(p, 1, 0, FAKE, None, one, e, None, FAKE, None) == INVALID        # null x_out
+    assert f(p, 1, 2, FAKE, None, one, e, FAKE, FAKE, None) == INVALID        # bad segment
+    assert f(p, 1, 1, FAKE, None, one, e, FAKE, None, None) == INVALID        # no condition frames
+    assert f(pc, 1, 1, FAKE, None, one, e, FAKE, FAKE, None) == INVALID       # means of cond
+    assert f(p, 1, 0, FAKE, None, ctypes.c_float(1.0), e, FAKE, FAKE, None) == INVALID
+    assert f(p, 1, 0, FAKE, None, ctypes.c_float(float("inf")), e, FAKE, FAKE, None) == INVALID
+    assert f(p, 1, 0, FAKE, None, one, ctypes.c_float(0.0), FAKE, FAKE, None) == INVALID
+    assert f(p, 1, 0, FAKE, None, one, ctypes.c_float(float("nan")), FAKE, FAKE, None) == INVALID
+    assert f(p, 7, 0, FAKE, None, one, e, FAKE, FAKE, None) == INVALID        # dtype
+    assert f(ctypes.byref(_p(T=7)), 1, 0, FAKE, None, one, e, FAKE, FAKE, None) == SHAPE

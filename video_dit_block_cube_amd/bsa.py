@@ -93,6 +93,7 @@ def lib() -> ctypes.CDLL:
         vp, i32, sz, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t, ctypes.c_float
         sigs = {
             "bsa_block_pool": (i32, [P, i32, vp, vp, vp]),
+            "bsa_qk_prologue": (i32, [P, i32, i32, vp, vp, f32, f32, vp, vp, vp]),
             "bsa_select_topr": (i32, [P, vp, vp, i32, vp, vp, vp]),
             "bsa_sparse_attn_fwd": (i32, [P, i32, vp, vp, vp, vp, vp, vp, i32, f32, vp, vp, vp,
                                           sz, vp]),
@@ -176,6 +177,31 @@ def bsa_block_pool(p: Problem, x: torch.Tensor, out: torch.Tensor | None = None)
                                      torch.float32),
                                 _stream(x)))
     return out
+
+
+def bsa_qk_prologue(p: Problem, x: torch.Tensor, gamma: torch.Tensor | None = None,
+                    rope_theta: float = 10000.0, eps: float = 1e-6, segment: int = 0,
+                    out: torch.Tensor | None = None, with_mean: bool = True,
+                    mean: torch.Tensor | None = None):
+    """RMS normalisation + 3D RoPE of one segment of q or k -> (x_out, cube means or None).
+
+    segment 0: x [B, Nq, Hh, D] (noise frames); 1: x [B, cond_T*H*W, Hh, D] (condition frames,
+    no means).  out may be x itself (in place)."""
+    n = p.Nq if segment == 0 else p.cond_T * p.H * p.W
+    shape_x = (p.batch, n, p.heads, p.head_dim)
+    if out is None:
+        out = torch.empty_like(x)
+    if segment == 0 and with_mean and mean is None:
+        mean = torch.empty((p.batch, p.heads, p.nbq, p.head_dim), dtype=torch.float32,
+                           device=x.device)
+    if segment != 0 or not with_mean:
+        mean = None
+    _check(lib().bsa_qk_prologue(
+        ctypes.byref(p.c_struct()), _dtype_code(x), segment, _ptr(x, "x", shape_x),
+        _ptr(gamma, "gamma", (p.head_dim,), torch.float32), rope_theta, eps,
+        _ptr(out, "x_out", shape_x, x.dtype),
+        _ptr(mean, "x_mean", (p.batch, p.heads, p.nbq, p.head_dim), torch.float32), _stream(x)))
+    return out, mean
 
 
 def bsa_select_topr(p: Problem, q_mean: torch.Tensor, k_mean: torch.Tensor, r: int,

@@ -179,6 +179,36 @@ bsa_status_t bsa_block_pool(const bsa_problem_t* p, bsa_dtype_t dtype, const voi
   });
 }
 
+bsa_status_t bsa_qk_prologue(const bsa_problem_t* p, bsa_dtype_t dtype, int32_t segment,
+                             const void* x, const float* gamma, float rope_theta, float eps,
+                             void* x_out, float* x_mean, hipStream_t stream) {
+  return guarded([&]() -> bsa_status_t {
+    Geom g;
+    bsa_status_t st = check_problem(p, &g);
+    if (st != BSA_OK) return st;
+    if ((st = check_dtype(dtype)) != BSA_OK) return st;
+    if (!x || !x_out) return fail(BSA_ERR_INVALID_ARG, "x and x_out must be non-NULL");
+    if (segment != 0 && segment != 1) return fail(BSA_ERR_INVALID_ARG, "segment must be 0 or 1");
+    if (segment == 1 && g.condT == 0)
+      return fail(BSA_ERR_INVALID_ARG, "segment 1 needs condition frames (cond_T > 0)");
+    if (segment == 1 && x_mean)
+      return fail(BSA_ERR_INVALID_ARG, "x_mean must be NULL for the condition segment");
+    if (!(std::isfinite(rope_theta) && rope_theta > 1.0f))
+      return fail(BSA_ERR_INVALID_ARG, "rope_theta must be finite and > 1");
+    if (!(std::isfinite(eps) && eps > 0.0f))
+      return fail(BSA_ERR_INVALID_ARG, "eps must be finite and > 0");
+    const Geom seg = segment == 0 ? noise_only(g)
+                                  : make_geom(g.B, g.Hh, g.D, g.condT, g.H, g.W, g.ct, g.ch,
+                                              g.cw, 0);
+    Stages stages(stream);
+    st = hip_status(launch_prologue(seg, segment == 0 ? g.condT : 0, dtype == BSA_BF16, x, gamma,
+                                    rope_theta, eps, x_out, x_mean, stream),
+                    "prologue launch");
+    stages.done("qk_prologue");
+    return st;
+  });
+}
+
 bsa_status_t bsa_select_topr(const bsa_problem_t* p, const float* q_mean, const float* k_mean,
                              int32_t r, int32_t* idx, uint8_t* mask, hipStream_t stream) {
   return guarded([&]() -> bsa_status_t {

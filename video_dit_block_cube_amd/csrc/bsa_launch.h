@@ -13,6 +13,12 @@ namespace bsa {
 // k_pool.hip: per-cube mean of a [B, Nq, Hh, D] tensor -> [B, Hh, nbq, D] fp32.
 hipError_t launch_pool(const Geom& g, bool bf16, const void* x, float* out, hipStream_t s);
 
+// k_prologue.hip: RMS normalisation + 3D RoPE of one segment (seg = its own geometry, frames
+// starting at grid time t_offset) and, when y_mean is non-null, the cube means of the result.
+hipError_t launch_prologue(const Geom& seg, int t_offset, bool bf16, const void* x,
+                           const float* gamma, float rope_theta, float eps, void* y,
+                           float* y_mean, hipStream_t s);
+
 // k_select.hip: block scores + forced set + top-r -> idx (ascending rows) and optional mask.
 hipError_t launch_select(const Geom& g, const float* qm, const float* km, int r_eff, int k_sel,
                          int32_t* idx, uint8_t* mask, hipStream_t s);
