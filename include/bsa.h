@@ -85,7 +85,7 @@ bsa_status_t bsa_block_pool(const bsa_problem_t* p, bsa_dtype_t dtype, const voi
                             float* x_mean, hipStream_t stream);
 
 /* Attention prologue fused with the cube pool: QK RMS normalisation (RMSNorm + QKNorm) and 3D
- * rotary position embedding over time, height and width (youleyou page, section "三、模型架构";
+ * rotary position embedding over time, height and width (xugj520 page, section "三、模型架构";
  * ai-news-5min-kr deep dive, layer table row for the positional encoding), then the per-cube
  * means of the result, in one pass over x.  The pages give no formula; per (token, head):
  *   y = x / sqrt(mean_d x^2 + eps) * gamma[d], then channel pairs (2i, 2i+1) of the time, height

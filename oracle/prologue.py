@@ -5,11 +5,12 @@ only tests/, __graft_entry__.smoke() and bench.py's CPU-baseline leg use it.  It
 table or helper with the HIP kernels and imports nothing from them.
 
 What the pages fix: every 3D self-attention layer of the DiT normalises its queries and keys
-(RMSNorm + QKNorm, "LongCat-Video视频生成模型发布 迈出世界模型探索第一步", youleyou, section
-"三、模型架构") and encodes position with rotary embeddings extended to the three axes time,
-height and width ("3D RoPE": same section; "LongCat-Video deep dive", ai-news-5min-kr, the layer
-table row for the positional encoding; "LongCat : Generate 1 minute long AI videos with this
-model", Data Science in Your Pocket, the 3D attention paragraph).  The pages give no formula, so
+(RMSNorm + QKNorm, "美团LongCat-Video揭秘：13.6B参数长视频生成模型如何终结画面漂移？",
+xugj520, section "三、模型架构：Diffusion Transformer 的高维协奏") and encodes position with
+rotary embeddings extended to the three axes time, height and width ("3D RoPE": same section;
+"LongCat-Video deep dive", ai-news-5min-kr, the layer table row for the positional encoding;
+"LongCat : Generate 1 minute long AI videos with this model", Data Science in Your Pocket, the
+3D attention paragraph).  The pages give no formula, so
 the readings below are the plainest ones:
 
   * normalisation: y = x / sqrt(mean_d x^2 + eps) * gamma over the head dimension, per (token,
@@ -22,8 +23,9 @@ the readings below are the plainest ones:
     token's integer coordinate on that axis of the full latent grid (condition frames first, so
     noise frame f sits at time position cond_T + f).
 
-Parity for these readings is pinned by tests/test_oracle_prologue.py against closed forms and a
-complex-number restatement, not against the pages (which print no values).
+These readings are pinned by tests/test_oracle_prologue.py against mathematics, not against the
+pages (which print no values): explicit rotations of unit vectors, group and relative-position
+properties of rotations, and exact properties of RMS normalisation.
 """
 from __future__ import annotations
 

@@ -2,9 +2,9 @@
 // position embedding and the per-cube means that feed block selection, in one HBM pass.
 //
 // Every 3D self-attention layer normalises its queries and keys and encodes position with rotary
-// embeddings over the three axes time, height and width ("LongCat-Video视频生成模型发布 迈出世界
-// 模型探索第一步", youleyou, section "三、模型架构"; "LongCat-Video deep dive", ai-news-5min-kr,
-// the layer table row for the positional encoding).  The pages give no formula; the kernel
+// embeddings over the three axes time, height and width ("美团LongCat-Video揭秘：13.6B参数长视频
+// 生成模型如何终结画面漂移？", xugj520, section "三、模型架构：Diffusion Transformer 的高维协奏";
+// "LongCat-Video deep dive", ai-news-5min-kr, the layer table row for the positional encoding).  The pages give no formula; the kernel
 // computes, per (token, head):
 //   y = x / sqrt(mean_d x^2 + eps) * gamma,  then channel pairs (2i, 2i+1) of the time, height and
 //   width blocks (widths D - 4*floor(D/6), 2*floor(D/6), 2*floor(D/6)) rotated by
