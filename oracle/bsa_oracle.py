@@ -23,7 +23,8 @@ What it computes, step by step, in the order the LongCat-Video pages describe th
      质量全程在线"; Data Science in Your Pocket, "The core idea: one model for all video tasks")
                                                                       -> attn_fwd_rows (cache),
                                                                          full_block_causal_fwd
-  6. backward for training (meituan.com talk, section 2.2)             -> attn_bwd
+  6. backward for training (meituan.com talk, section 2.2), including the gradients of the
+     cached condition K/V for continuation training                   -> attn_bwd
 
 Readings where the pages are silent (pool = arithmetic mean, score = D^-1/2 <q_mean, k_mean>,
 self forced and r counted on top of it, ties to the lower cube id, raster cube order, no gradient
@@ -282,17 +283,24 @@ def sparse_attn_fwd(q, k, v, k_cache, v_cache, idx, p: Problem, scale: float, he
 # Step 6: backward, selection held constant (the top-r choice is discrete and gets no gradient).
 # Reading: Delta is computed from the oracle's own fp64 output.
 # --------------------------------------------------------------------------------------------
-def attn_bwd(q, k, v, dO, idx, p: Problem, scale: float, rows=None, key_cubes=None):
-    """Gradients of L = <dO, O> with respect to q, k, v (cond_T must be 0).
+def attn_bwd(q, k, v, dO, idx, p: Problem, scale: float, rows=None, key_cubes=None,
+             k_cache=None, v_cache=None):
+    """Gradients of L = <dO, O> with respect to q, k, v and, with condition frames, the cached
+    condition k_cache, v_cache (the continuation mode: the cache is read by every noise query).
 
     rows:      None for every query cube, else an iterable of (b, h, i) whose dQ is wanted.
-    key_cubes: None for every key cube, else an iterable of (b, h, j) whose dK, dV are wanted.
-    Returns (dQ, dK, dV) as dicts keyed like rows / key_cubes ([c, D] fp64 each) when either
-    selector is given, else full fp64 arrays [B, Nq, Hh, D]."""
+    key_cubes: None for every key cube, else an iterable of (b, h, j) whose dK, dV are wanted,
+               j a key cube id (condition cubes 0..nbc-1 first, then noise cubes).
+    Full mode (no selector): fp64 arrays dQ, dK, dV [B, Nq, Hh, D], plus dK_cache, dV_cache
+    [B, Nc, Hh, D] when cond_T > 0.  Selector mode: dicts keyed like rows / key_cubes ([c, D]
+    fp64 each; condition key cubes sit in the dK, dV dicts under their ids), plus (None, None)
+    when cond_T > 0."""
     check_problem(p)
-    if p.cond_T != 0:
-        raise ProblemError("unsupported", "backward needs cond_T == 0")
+    cached = p.cond_T > 0
+    if cached and (k_cache is None or v_cache is None):
+        raise ProblemError("invalid", "condition frames need k_cache and v_cache")
     qt = noise_cube_tokens(p)
+    ct_ = cond_cube_tokens(p) if cached else None
     c, D = p.c, p.head_dim
     full = rows is None and key_cubes is None
     want_rows = None if rows is None else set(map(tuple, rows))
@@ -301,6 +309,8 @@ def attn_bwd(q, k, v, dO, idx, p: Problem, scale: float, rows=None, key_cubes=No
         dQ = np.zeros((p.batch, p.Nq, p.heads, D))
         dK = np.zeros_like(dQ)
         dV = np.zeros_like(dQ)
+        dKc = np.zeros((p.batch, p.Nc, p.heads, D)) if cached else None
+        dVc = np.zeros_like(dKc) if cached else None
     else:
         dQ, dK, dV = {}, {}, {}
         for key in want_cols or ():
@@ -317,8 +327,8 @@ def attn_bwd(q, k, v, dO, idx, p: Problem, scale: float, rows=None, key_cubes=No
                     continue
                 Qi = np.asarray(q[b, qt[i], h, :], dtype=np.float64)
                 dOi = np.asarray(dO[b, qt[i], h, :], dtype=np.float64)
-                Ks = _gather_keys(k, None, sel, b, h, p)
-                Vs = _gather_keys(v, None, sel, b, h, p)
+                Ks = _gather_keys(k, k_cache, sel, b, h, p)
+                Vs = _gather_keys(v, v_cache, sel, b, h, p)
                 s = scale * (Qi @ Ks.T)
                 m = s.max(axis=1, keepdims=True)
                 e = np.exp(s - m)
@@ -333,8 +343,13 @@ def attn_bwd(q, k, v, dO, idx, p: Problem, scale: float, rows=None, key_cubes=No
                 if full:
                     dQ[b, qt[i], h, :] += scale * (dS @ Ks)
                     for pos, j in enumerate(sel):
-                        dK[b, qt[int(j)], h, :] += dKs[pos * c:(pos + 1) * c]
-                        dV[b, qt[int(j)], h, :] += dVs[pos * c:(pos + 1) * c]
+                        j = int(j)
+                        if j < p.nbc:
+                            dKc[b, ct_[j], h, :] += dKs[pos * c:(pos + 1) * c]
+                            dVc[b, ct_[j], h, :] += dVs[pos * c:(pos + 1) * c]
+                        else:
+                            dK[b, qt[j - p.nbc], h, :] += dKs[pos * c:(pos + 1) * c]
+                            dV[b, qt[j - p.nbc], h, :] += dVs[pos * c:(pos + 1) * c]
                 else:
                     if need_q:
                         dQ[(b, h, i)] = scale * (dS @ Ks)
@@ -342,7 +357,11 @@ def attn_bwd(q, k, v, dO, idx, p: Problem, scale: float, rows=None, key_cubes=No
                         key = (b, h, int(sel[pos]))
                         dK[key] += dKs[pos * c:(pos + 1) * c]
                         dV[key] += dVs[pos * c:(pos + 1) * c]
-    return dQ, dK, dV
+    if not cached:
+        return dQ, dK, dV
+    if full:
+        return dQ, dK, dV, dKc, dVc
+    return dQ, dK, dV, None, None
 
 
 def delta_rows(o: np.ndarray, dO: np.ndarray) -> np.ndarray:

@@ -133,3 +133,81 @@ def test_transpose_selection_and_delta():
     O, _ = orc.sparse_attn_fwd(x["q"], x["k"], x["v"], None, None, idx, p, 0.125)
     d = orc.delta_rows(O, dO)
     np.testing.assert_allclose(d[0, 0, 17], float(np.dot(O[0, 17, 0], dO[0, 17, 0])), atol=1e-14)
+
+
+# ---------------------------------------------------------------------------------------------
+# Continuation mode: gradients of the cached condition K/V.
+# ---------------------------------------------------------------------------------------------
+def _tiny_cached(seed=5):
+    p = orc.Problem(batch=1, heads=2, head_dim=64, T=4, H=4, W=4, cube_t=2, cube_h=2, cube_w=2,
+                    cond_T=2)
+    rng = np.random.default_rng(seed)
+    shp_n = (1, p.Nq, 2, 64)
+    shp_c = (1, p.Nc, 2, 64)
+    x = {"q": rng.standard_normal(shp_n), "k": rng.standard_normal(shp_n),
+         "v": rng.standard_normal(shp_n), "k_cache": rng.standard_normal(shp_c),
+         "v_cache": rng.standard_normal(shp_c)}
+    dO = rng.standard_normal(shp_n)
+    qm, km = orc.block_pool(x["q"], p), orc.block_pool(x["k"], p)
+    idx, _ = orc.select_topr(qm, km, p, 1)
+    return p, x, dO, idx
+
+
+def _loss_cached(x, dO, idx, p, scale):
+    O, _ = orc.sparse_attn_fwd(x["q"], x["k"], x["v"], x["k_cache"], x["v_cache"], idx, p, scale)
+    return float(np.sum(O * dO))
+
+
+def test_cache_gradients_finite_differences():
+    p, x, dO, idx = _tiny_cached()
+    scale = 1 / math.sqrt(p.head_dim)
+    gq, gk, gv, gkc, gvc = orc.attn_bwd(x["q"], x["k"], x["v"], dO, idx, p, scale,
+                                         k_cache=x["k_cache"], v_cache=x["v_cache"])
+    grads = {"q": gq, "k": gk, "v": gv, "k_cache": gkc, "v_cache": gvc}
+    rng = np.random.default_rng(78)
+    h = 1e-5
+    for name in grads:
+        for _ in range(8):
+            d = rng.standard_normal(x[name].shape)
+            xp = dict(x); xp[name] = x[name] + h * d
+            xm = dict(x); xm[name] = x[name] - h * d
+            fd = (_loss_cached(xp, dO, idx, p, scale) - _loss_cached(xm, dO, idx, p, scale)) / (2 * h)
+            an = float(np.sum(grads[name] * d))
+            assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (name, fd, an)
+
+
+def test_cache_gradients_match_torch_autograd_block_causal_mask():
+    """Noise queries over [condition keys | noise keys] with the token-level mask of the
+    selection: torch float64 autograd through SDPA gives every gradient, cache ones included."""
+    p, x, dO, idx = _tiny_cached(6)
+    scale = 1 / math.sqrt(p.head_dim)
+    gq, gk, gv, gkc, gvc = orc.attn_bwd(x["q"], x["k"], x["v"], dO, idx, p, scale,
+                                         k_cache=x["k_cache"], v_cache=x["v_cache"])
+    qt, ct = orc.noise_cube_tokens(p), orc.cond_cube_tokens(p)
+    kfull = np.concatenate([x["k_cache"], x["k"]], axis=1)
+    vfull = np.concatenate([x["v_cache"], x["v"]], axis=1)
+    for h in range(p.heads):
+        mask = np.zeros((p.Nq, p.Nc + p.Nq), dtype=bool)
+        for i in range(p.nbq):
+            for j in idx[0, h, i]:
+                j = int(j)
+                cols = ct[j] if j < p.nbc else p.Nc + qt[j - p.nbc]
+                mask[np.ix_(qt[i], cols)] = True
+        rq, rk, rv = _autograd_ref(x["q"][:, :, h:h + 1], kfull[:, :, h:h + 1],
+                                   vfull[:, :, h:h + 1], dO[:, :, h:h + 1], scale, mask)
+        np.testing.assert_allclose(gq[:, :, h:h + 1], rq, atol=1e-12)
+        np.testing.assert_allclose(gkc[:, :, h:h + 1], rk[:, :p.Nc], atol=1e-12)
+        np.testing.assert_allclose(gk[:, :, h:h + 1], rk[:, p.Nc:], atol=1e-12)
+        np.testing.assert_allclose(gvc[:, :, h:h + 1], rv[:, :p.Nc], atol=1e-12)
+        np.testing.assert_allclose(gv[:, :, h:h + 1], rv[:, p.Nc:], atol=1e-12)
+
+
+def test_cache_gradient_invariants():
+    p, x, dO, idx = _tiny_cached(7)
+    scale = 1 / math.sqrt(p.head_dim)
+    _, gk, gv, gkc, gvc = orc.attn_bwd(x["q"], x["k"], x["v"], dO, idx, p, scale,
+                                        k_cache=x["k_cache"], v_cache=x["v_cache"])
+    np.testing.assert_allclose(gv.sum(axis=1) + gvc.sum(axis=1), dO.sum(axis=1), atol=1e-12)
+    np.testing.assert_allclose(gk.sum(axis=1) + gkc.sum(axis=1), 0.0, atol=1e-12)
+    # every noise query attends every condition cube, so every cache row gets gradient
+    assert np.all(np.abs(gvc).sum(axis=-1) > 0)
