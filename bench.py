@@ -293,11 +293,39 @@ def bench_continuation(bsa, synth, orc, torch, dev, args):
     avg = {k: float(np.mean(v)) for k, v in st.items()}
     f = 4.0 * p.batch * p.heads * p.Nq * (ks * p.c) * p.head_dim
     attn = avg.get("attn_fwd_mfma", float("nan"))
+    # backward with the condition-cache gradients (continuation training)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(4245)
+    d_o = torch.randn(t["q"].shape, generator=gen, device=dev,
+                      dtype=torch.float32).to(torch.bfloat16)
+    wsb = torch.empty(bsa.bsa_workspace_bytes(p, torch.bfloat16, ks, True), dtype=torch.uint8,
+                      device=dev)
+    grads = bsa.bsa_sparse_attn_bwd(p, t["q"], t["k"], t["v"], o, d_o, lse, idx, ks, scale,
+                                    workspace=wsb, k_cache=t["k_cache"], v_cache=t["v_cache"])
+    torch.cuda.synchronize()
+    evb = [bsa.StageEvents(8) for _ in range(3)]
+    for ev in evb:
+        with ev:
+            bsa.bsa_sparse_attn_bwd(p, t["q"], t["k"], t["v"], o, d_o, lse, idx, ks, scale,
+                                    dq=grads[0], dk=grads[1], dv=grads[2], workspace=wsb,
+                                    k_cache=t["k_cache"], v_cache=t["v_cache"],
+                                    dk_cache=grads[3], dv_cache=grads[4])
+    torch.cuda.synchronize()
+    sb: dict[str, list] = {}
+    for ev in evb:
+        for name, ms in ev.elapsed_all():
+            sb.setdefault(name, []).append(ms)
+    bavg = {k: round(float(np.mean(v)), 3) for k, v in sb.items()}
+    bwd_ms = sum(bavg.values())
     return {"workload": "720p-class continuation: 12 condition frames cached, top-r=72 noise "
                         "cubes + own cube + 720 condition cubes",
             "k_sel": ks, "tflop": round(f / 1e12, 3), "gather_ms": round(avg.get("gather_qkv", 0), 3),
             "attn_ms": round(attn, 3), "attn_tflops": round(f / (attn * 1e-3) / 1e12, 1),
-            "frac_peak": round(f / (attn * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+            "frac_peak": round(f / (attn * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "bwd_with_cache_grads": {
+                "ms": round(bwd_ms, 3), "stages_ms": bavg,
+                "tflop_effective": round(2.5 * f / 1e12, 3),
+                "tflops_effective": round(2.5 * f / (bwd_ms * 1e-3) / 1e12, 1)}}
 
 
 def _time_fwd(bsa, torch, p, t, r, reps=3):

@@ -144,20 +144,27 @@ bsa_status_t bsa_sparse_attn_fwd(const bsa_problem_t* p, bsa_dtype_t dtype, cons
                                  size_t ws_bytes, hipStream_t stream);
 
 /* Backward of bsa_sparse_attn_fwd with the selection held constant (the forward and backward
- * both ship, meituan.com talk, section 2.2).  With P = exp(scale*Q_i K_j^T - LSE_i):
+ * both ship, meituan.com talk, section 2.2; training with a condition cache is the continuation
+ * pre-training of section 2.1).  With P = exp(scale*Q_i K_j^T - LSE_i):
  *   dV_j += P^T dO_i;  dS = P o (dO_i V_j^T - Delta_i);  dQ_i += scale*dS K_j;
  *   dK_j += scale*dS^T Q_i;  Delta_i = rowsum(dO_i o O_i),  over every i and j in idx[b,h,i,:].
+ * Condition key cubes (id < nbc) are read from k_cache / v_cache and their dK_j, dV_j are written
+ * to dk_cache / dv_cache.
  *   q, k, v, o, d_o    device, [B, Nq, Hh, D] dtype (o, lse from the forward)
+ *   k_cache, v_cache   device, [B, Nc, Hh, D] dtype; NULL iff cond_T == 0
  *   lse                device, [B, Hh, Nq] fp32
  *   dq, dk, dv         device, [B, Nq, Hh, D] fp32, overwritten
+ *   dk_cache, dv_cache device, [B, Nc, Hh, D] fp32, overwritten; NULL iff cond_T == 0
  *   ws, ws_bytes       device workspace of at least bsa_workspace_bytes(p, dtype, k_sel, 1)
- * cond_T must be 0 (gradients of the condition cache are not produced): UNSUPPORTED otherwise.
+ * With cond_T > 0 only the bf16 MFMA path (64-token cubes) is implemented: UNSUPPORTED otherwise.
  * Errors: INVALID_ARG, SHAPE, UNSUPPORTED, WORKSPACE, HIP. */
 bsa_status_t bsa_sparse_attn_bwd(const bsa_problem_t* p, bsa_dtype_t dtype, const void* q,
-                                 const void* k, const void* v, const void* o, const void* d_o,
+                                 const void* k, const void* v, const void* k_cache,
+                                 const void* v_cache, const void* o, const void* d_o,
                                  const float* lse, const int32_t* idx, int32_t k_sel,
-                                 float softmax_scale, float* dq, float* dk, float* dv, void* ws,
-                                 size_t ws_bytes, hipStream_t stream);
+                                 float softmax_scale, float* dq, float* dk, float* dv,
+                                 float* dk_cache, float* dv_cache, void* ws, size_t ws_bytes,
+                                 hipStream_t stream);
 
 /* ---- helpers (host only, no HIP calls) ---- */
 

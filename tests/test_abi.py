@@ -101,12 +101,30 @@ def test_argument_errors(L):
     assert fwd(p, 1, FAKE, FAKE, FAKE, None, None, FAKE, 3, ctypes.c_float(float("nan")), FAKE,
                FAKE, FAKE, 1 << 40, None) == INVALID
     bwd = L.bsa_sparse_attn_bwd
-    assert bwd(pc, 1, *[FAKE] * 7, 5, ctypes.c_float(0.1), FAKE, FAKE, FAKE, FAKE, 1 << 40,
-               None) == UNSUPPORTED
-    assert bwd(p, 1, *[FAKE] * 7, 3, ctypes.c_float(0.1), FAKE, FAKE, FAKE, FAKE, 8,
-               None) == WORKSPACE
-    assert bwd(p, 1, *[FAKE] * 6, None, 3, ctypes.c_float(0.1), FAKE, FAKE, FAKE, FAKE, 1 << 40,
-               None) == INVALID
+    sc = ctypes.c_float(0.1)
+    # argument order: q, k, v, k_cache, v_cache, o, d_o, lse, idx, k_sel, scale,
+    #                 dq, dk, dv, dk_cache, dv_cache, ws, ws_bytes, stream
+    cache4 = [FAKE, FAKE]
+    # condition frames need all four cache tensors; without them none may be given
+    assert bwd(pc, 1, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, FAKE, FAKE, 5, sc,
+               FAKE, FAKE, FAKE, None, None, FAKE, 1 << 40, None) == INVALID
+    assert bwd(pc, 1, FAKE, FAKE, FAKE, *cache4, FAKE, FAKE, FAKE, FAKE, 5, sc,
+               FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 40, None) == INVALID
+    assert bwd(p, 1, FAKE, FAKE, FAKE, *cache4, FAKE, FAKE, FAKE, FAKE, 3, sc,
+               FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, None) == INVALID
+    # cache gradients exist on the bf16 MFMA path only
+    assert bwd(pc, 0, FAKE, FAKE, FAKE, *cache4, FAKE, FAKE, FAKE, FAKE, 5, sc,
+               FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, None) == UNSUPPORTED
+    assert bwd(p, 1, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, FAKE, FAKE, 3, sc,
+               FAKE, FAKE, FAKE, None, None, FAKE, 8, None) == WORKSPACE
+    assert bwd(p, 1, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, FAKE, None, 3, sc,
+               FAKE, FAKE, FAKE, None, None, FAKE, 1 << 40, None) == INVALID
+    # the condition-mode workspace covers K/V gathers over every key cube
+    big = bsa.Problem(1, 32, 128, 24, 48, 80, 4, 4, 4, cond_T=12)
+    plain = bsa.Problem(1, 32, 128, 12, 48, 80, 4, 4, 4)
+    import torch
+    assert bsa.bsa_workspace_bytes(big, torch.bfloat16, 793, True) > \
+        bsa.bsa_workspace_bytes(plain, torch.bfloat16, 73, True)
     assert L.bsa_last_error()  # a message is kept for the last failure
 
 

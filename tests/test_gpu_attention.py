@@ -255,3 +255,78 @@ def test_bwd_full_size_sampled():
     dO64 = x["dO"].astype(np.float64)
     np.testing.assert_allclose(dv.sum(axis=1), dO64.sum(axis=1), atol=0.5, rtol=1e-2)
     assert np.abs(dk.astype(np.float64).sum(axis=1)).max() < 0.5
+
+
+# ---------------------------------------------------------------------------------------------
+# Backward with the condition cache (continuation training): cache gradients included.
+# ---------------------------------------------------------------------------------------------
+def _cached_bwd_case(over, r, seed=4243):
+    import torch
+    w = synth.workload(4, **over)
+    x = synth.make_inputs(w)
+    rng = np.random.default_rng(seed)
+    dO = rng.standard_normal(x["q"].shape).astype(np.float32)
+    dO = synth.round_to_bf16(dO)
+    p, op, idx, t = _setup(w, x, r)
+    t["dO"] = to_dev(dO, w.dtype)
+    ks = orc.num_selected(op, r)
+    scale = scale_of(op)
+    o, lse = _fwd(p, t, idx, ks, scale)
+    got = bsa.bsa_sparse_attn_bwd(p, t["q"], t["k"], t["v"], o, t["dO"], lse, _idx_dev(idx), ks,
+                                  scale, k_cache=t["k_cache"], v_cache=t["v_cache"])
+    torch.cuda.synchronize()
+    return w, x, dO, op, idx, scale, [a.cpu().numpy() for a in got]
+
+
+@pytest.mark.parametrize("over, r", [
+    (dict(batch=2, heads=2, T=12, H=8, W=16, cond_T=4), 3),
+    (dict(heads=2, head_dim=64, T=12, H=8, W=16, cond_T=8), 2),
+    (dict(heads=2, T=24, H=16, W=32, cond_T=12), 9),          # 96 + 96 cubes, k_sel = 106
+])
+def test_bwd_condition_cache(over, r):
+    print_case(f"bwd cached {over} r={r}")
+    w, x, dO, op, idx, scale, got = _cached_bwd_case(over, r)
+    ref = orc.attn_bwd(x["q"], x["k"], x["v"], dO, idx, op, scale, k_cache=x["k_cache"],
+                       v_cache=x["v_cache"])
+    for name, g, rf in zip(("dQ", "dK", "dV", "dK_cache", "dV_cache"), got, ref):
+        assert_close(g, rf, "bf16", name)
+
+
+def test_bwd_condition_cache_full_size_sampled():
+    """720p-class continuation (12 cached condition frames, top-r = 72): sampled dQ rows against
+    the oracle, and every key's gradient through the full-size sums over noise and cache keys."""
+    w = synth.workload(4)
+    print_case("bwd cached full size 720p continuation")
+    import torch
+    x = synth.make_inputs(w)
+    rng = np.random.default_rng(4244)
+    dO = synth.round_to_bf16(rng.standard_normal(x["q"].shape).astype(np.float32))
+    p = bsa.Problem(**w.shape_dict)
+    op = orc.Problem(**w.shape_dict)
+    t = {k: to_dev(v, w.dtype) for k, v in x.items() if k != "dO"}
+    t["dO"] = to_dev(dO, w.dtype)
+    idx_d = _gpu_selection(w, t, p)
+    ks = orc.num_selected(op, w.r)
+    scale = scale_of(op)
+    o, lse = bsa.bsa_sparse_attn_fwd(p, t["q"], t["k"], t["v"], idx_d, ks, scale, t["k_cache"],
+                                     t["v_cache"])
+    dq, dk, dv, dkc, dvc = bsa.bsa_sparse_attn_bwd(p, t["q"], t["k"], t["v"], o, t["dO"], lse,
+                                                   idx_d, ks, scale, k_cache=t["k_cache"],
+                                                   v_cache=t["v_cache"])
+    idx = idx_d.cpu().numpy()
+    dq, dk, dv, dkc, dvc = (a.cpu().numpy() for a in (dq, dk, dv, dkc, dvc))
+    for a in (dq, dk, dv, dkc, dvc):
+        assert np.all(np.isfinite(a))
+    rows = [(0, 0, 0), (0, 15, 359), (0, 31, 719)]
+    rq = orc.attn_bwd(x["q"], x["k"], x["v"], dO, idx, op, scale, rows=rows,
+                      k_cache=x["k_cache"], v_cache=x["v_cache"])[0]
+    toks = orc.noise_cube_tokens(op)
+    assert_close(np.stack([dq[b, toks[i], h] for (b, h, i) in rows]),
+                 np.stack([rq[k] for k in rows]), "bf16", "dQ")
+    dO64 = dO.astype(np.float64)
+    np.testing.assert_allclose(dv.sum(axis=1) + dvc.sum(axis=1), dO64.sum(axis=1), atol=0.5,
+                               rtol=1e-2)
+    assert np.abs(dk.astype(np.float64).sum(axis=1) + dkc.astype(np.float64).sum(axis=1)).max() \
+        < 0.5
+    # every cache row receives gradient (all noise queries attend every condition cube)
+    assert np.all(np.abs(dvc).sum(axis=-1) > 0)

@@ -97,8 +97,8 @@ def lib() -> ctypes.CDLL:
             "bsa_select_topr": (i32, [P, vp, vp, i32, vp, vp, vp]),
             "bsa_sparse_attn_fwd": (i32, [P, i32, vp, vp, vp, vp, vp, vp, i32, f32, vp, vp, vp,
                                           sz, vp]),
-            "bsa_sparse_attn_bwd": (i32, [P, i32, vp, vp, vp, vp, vp, vp, vp, i32, f32, vp, vp,
-                                          vp, vp, sz, vp]),
+            "bsa_sparse_attn_bwd": (i32, [P, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, f32,
+                                          vp, vp, vp, vp, vp, vp, sz, vp]),
             "bsa_num_selected": (i32, [P, i32]),
             "bsa_workspace_bytes": (sz, [P, i32, i32, i32]),
             "bsa_status_string": (ctypes.c_char_p, [i32]),
@@ -260,23 +260,37 @@ def bsa_sparse_attn_fwd(p: Problem, q, k, v, idx, k_sel: int, softmax_scale: flo
 
 def bsa_sparse_attn_bwd(p: Problem, q, k, v, o, d_o, lse, idx, k_sel: int,
                         softmax_scale: float | None = None, dq=None, dk=None, dv=None,
-                        workspace=None):
-    """-> (dq, dk, dv) fp32 [B, Nq, Hh, D]."""
+                        workspace=None, k_cache=None, v_cache=None, dk_cache=None,
+                        dv_cache=None):
+    """-> (dq, dk, dv) fp32 [B, Nq, Hh, D]; with condition frames (k_cache, v_cache given)
+    -> (dq, dk, dv, dk_cache, dv_cache), the last two [B, Nc, Hh, D]."""
     scale = 1.0 / math.sqrt(p.head_dim) if softmax_scale is None else float(softmax_scale)
     shp = (p.batch, p.Nq, p.heads, p.head_dim)
+    shc = (p.batch, p.Nc, p.heads, p.head_dim)
     dt = q.dtype
     dq = torch.empty(shp, dtype=torch.float32, device=q.device) if dq is None else dq
     dk = torch.empty(shp, dtype=torch.float32, device=q.device) if dk is None else dk
     dv = torch.empty(shp, dtype=torch.float32, device=q.device) if dv is None else dv
+    cached = k_cache is not None
+    if cached:
+        dk_cache = torch.empty(shc, dtype=torch.float32, device=q.device) \
+            if dk_cache is None else dk_cache
+        dv_cache = torch.empty(shc, dtype=torch.float32, device=q.device) \
+            if dv_cache is None else dv_cache
     ws, need = _workspace(p, dt, k_sel, True, q.device, workspace)
     _check(lib().bsa_sparse_attn_bwd(
         ctypes.byref(p.c_struct()), _dtype_code(q), _ptr(q, "q", shp, dt), _ptr(k, "k", shp, dt),
-        _ptr(v, "v", shp, dt), _ptr(o, "o", shp, dt), _ptr(d_o, "d_o", shp, dt),
+        _ptr(v, "v", shp, dt), _ptr(k_cache, "k_cache", shc, dt),
+        _ptr(v_cache, "v_cache", shc, dt), _ptr(o, "o", shp, dt), _ptr(d_o, "d_o", shp, dt),
         _ptr(lse, "lse", (p.batch, p.heads, p.Nq), torch.float32),
         _ptr(idx, "idx", (p.batch, p.heads, p.nbq, k_sel), torch.int32), int(k_sel),
         ctypes.c_float(scale), _ptr(dq, "dq", shp, torch.float32),
         _ptr(dk, "dk", shp, torch.float32), _ptr(dv, "dv", shp, torch.float32),
+        _ptr(dk_cache if cached else None, "dk_cache", shc, torch.float32),
+        _ptr(dv_cache if cached else None, "dv_cache", shc, torch.float32),
         _ptr(ws, "workspace"), ctypes.c_size_t(ws.numel()), _stream(q)))
+    if cached:
+        return dq, dk, dv, dk_cache, dv_cache
     return dq, dk, dv
 
 

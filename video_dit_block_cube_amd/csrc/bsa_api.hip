@@ -99,6 +99,11 @@ bsa_status_t hip_status(hipError_t e, const char* what) {
 }
 
 // Workspace layout of the backward (and of the forward for the MFMA path).
+// The query-only view of a problem (no condition segment): gathers of Q cover the noise cubes.
+Geom noise_only(const Geom& g) {
+  return make_geom(g.B, g.Hh, g.D, g.nT, g.H, g.W, g.ct, g.ch, g.cw, 0);
+}
+
 struct BwdWs {
   size_t delta, lse, ld, bits, off, list, g_qr, g_dr, g_kr, g_vr, total;
 };
@@ -119,11 +124,12 @@ BwdWs bwd_layout(const Geom& g, bool mfma, int k_sel) {
   w.off = take((size_t)g.B * g.Hh * (g.nbk + 1) * sizeof(int32_t));
   w.list = take((size_t)g.B * g.Hh * g.nbq * (size_t)k_sel * sizeof(int32_t));
   if (mfma) {
-    const size_t gb = gather_bytes(g, true);
-    w.g_qr = take(gb);
-    w.g_dr = take(gb);
-    w.g_kr = take(gb);
-    w.g_vr = take(gb);
+    const size_t gq = gather_bytes(noise_only(g), true);  // Q, dO: the query cubes
+    const size_t gk = gather_bytes(g, true);              // K, V: every key cube
+    w.g_qr = take(gq);
+    w.g_dr = take(gq);
+    w.g_kr = take(gk);
+    w.g_vr = take(gk);
   }
   w.total = at;
   return w;
@@ -134,11 +140,6 @@ BwdWs bwd_layout(const Geom& g, bool mfma, int k_sel) {
 int fwd_splits(const Geom& g, int k_sel) {
   const char* env = std::getenv("BSA_FWD_SPLITS");
   return fwd_split_ranges(g, k_sel, env ? std::atoi(env) : -1);
-}
-
-// The query-only view of a problem (no condition segment): gathers of Q cover the noise cubes.
-Geom noise_only(const Geom& g) {
-  return make_geom(g.B, g.Hh, g.D, g.nT, g.H, g.W, g.ct, g.ch, g.cw, 0);
 }
 
 // Forward workspace (MFMA path): K rows + V^T over all nbk key cubes, Q rows over the nbq query
@@ -286,22 +287,31 @@ bsa_status_t bsa_sparse_attn_fwd(const bsa_problem_t* p, bsa_dtype_t dtype, cons
 }
 
 bsa_status_t bsa_sparse_attn_bwd(const bsa_problem_t* p, bsa_dtype_t dtype, const void* q,
-                                 const void* k, const void* v, const void* o, const void* d_o,
+                                 const void* k, const void* v, const void* k_cache,
+                                 const void* v_cache, const void* o, const void* d_o,
                                  const float* lse, const int32_t* idx, int32_t k_sel,
-                                 float softmax_scale, float* dq, float* dk, float* dv, void* ws,
-                                 size_t ws_bytes, hipStream_t stream) {
+                                 float softmax_scale, float* dq, float* dk, float* dv,
+                                 float* dk_cache, float* dv_cache, void* ws, size_t ws_bytes,
+                                 hipStream_t stream) {
   return guarded([&]() -> bsa_status_t {
     Geom g;
     bsa_status_t st = check_problem(p, &g);
     if (st != BSA_OK) return st;
     if ((st = check_dtype(dtype)) != BSA_OK) return st;
-    if (g.condT != 0)
-      return fail(BSA_ERR_UNSUPPORTED, "backward needs cond_T == 0 (no condition-cache grads)");
     if ((st = check_ksel(g, k_sel)) != BSA_OK) return st;
     if (!q || !k || !v || !o || !d_o || !lse || !idx || !dq || !dk || !dv)
       return fail(BSA_ERR_INVALID_ARG, "every tensor pointer must be non-NULL");
+    const bool cached = g.condT > 0;
+    const bool any_cache = k_cache || v_cache || dk_cache || dv_cache;
+    const bool all_cache = k_cache && v_cache && dk_cache && dv_cache;
+    if (cached ? !all_cache : any_cache)
+      return fail(BSA_ERR_INVALID_ARG,
+                  "k_cache, v_cache, dk_cache, dv_cache are required iff cond_T > 0");
     if (!std::isfinite(softmax_scale)) return fail(BSA_ERR_INVALID_ARG, "softmax_scale not finite");
     const bool mfma = use_mfma(g, dtype);
+    if (cached && !mfma)
+      return fail(BSA_ERR_UNSUPPORTED,
+                  "condition-cache gradients need the bf16 MFMA path (64-token cubes)");
     const BwdWs w = bwd_layout(g, mfma, k_sel);
     if (!ws || ws_bytes < w.total)
       return fail(BSA_ERR_WORKSPACE, "workspace smaller than bsa_workspace_bytes()");
@@ -322,21 +332,23 @@ bsa_status_t bsa_sparse_attn_bwd(const bsa_problem_t* p, bsa_dtype_t dtype, cons
     stages.done("bwd_prep");
     if (mfma) {
       auto at = [&](size_t o2) { return reinterpret_cast<bf16_t*>(base + o2); };
-      st = hip_status(launch_gather(g, q, nullptr, GATHER_ROW, at(w.g_qr), nullptr, stream),
+      const Geom gq = noise_only(g);
+      st = hip_status(launch_gather(gq, q, nullptr, GATHER_ROW, at(w.g_qr), nullptr, stream),
                       "gather Q");
       if (st != BSA_OK) return st;
-      st = hip_status(launch_gather(g, d_o, nullptr, GATHER_ROW, at(w.g_dr), nullptr, stream),
+      st = hip_status(launch_gather(gq, d_o, nullptr, GATHER_ROW, at(w.g_dr), nullptr, stream),
                       "gather dO");
       if (st != BSA_OK) return st;
-      st = hip_status(launch_gather(g, k, nullptr, GATHER_ROW, at(w.g_kr), nullptr, stream),
+      st = hip_status(launch_gather(g, k, k_cache, GATHER_ROW, at(w.g_kr), nullptr, stream),
                       "gather K");
       if (st != BSA_OK) return st;
-      st = hip_status(launch_gather(g, v, nullptr, GATHER_ROW, at(w.g_vr), nullptr, stream),
+      st = hip_status(launch_gather(g, v, v_cache, GATHER_ROW, at(w.g_vr), nullptr, stream),
                       "gather V");
       if (st != BSA_OK) return st;
       stages.done("gather_qkv_do");
       st = hip_status(launch_bwd_dkdv_mfma(g, at(w.g_kr), at(w.g_vr), at(w.g_qr), at(w.g_dr),
-                                           ld_c, off, list, softmax_scale, dk, dv, stream),
+                                           ld_c, off, list, softmax_scale, dk, dv, dk_cache,
+                                           dv_cache, stream),
                       "dK/dV launch");
       if (st != BSA_OK) return st;
       stages.done("bwd_dkdv_mfma");

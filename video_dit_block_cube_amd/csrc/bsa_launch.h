@@ -67,6 +67,8 @@ hipError_t launch_fwd_mfma(const Geom& g, const bf16_t* q_row, const bf16_t* k_r
 
 // k_bwd_mfma.hip: bf16 MFMA backward kernels for c == 64, D in {64, 128}; every operand comes
 // from the ROW gather layout (transposed operands are read from LDS with ds_read_b64_tr_b16).
+// k_row / v_row cover all nbk key cubes (condition cubes first), q_row / do_row the nbq query
+// cubes; dK/dV of condition key cubes go to dk_cache / dv_cache ([B, Nc, Hh, D]).
 hipError_t launch_bwd_dq_mfma(const Geom& g, const bf16_t* q_row, const bf16_t* do_row,
                               const bf16_t* k_row, const bf16_t* v_row, const float2* ld_c,
                               const int32_t* idx, int k_sel, float scale, float* dq,
@@ -74,6 +76,7 @@ hipError_t launch_bwd_dq_mfma(const Geom& g, const bf16_t* q_row, const bf16_t* 
 hipError_t launch_bwd_dkdv_mfma(const Geom& g, const bf16_t* k_row, const bf16_t* v_row,
                                 const bf16_t* q_row, const bf16_t* do_row, const float2* ld_c,
                                 const int32_t* csr_off, const int32_t* csr_list, float scale,
-                                float* dk, float* dv, hipStream_t s);
+                                float* dk, float* dv, float* dk_cache, float* dv_cache,
+                                hipStream_t s);
 
 }  // namespace bsa

@@ -238,8 +238,9 @@ __global__ __launch_bounds__(64) void bwd_dq_mfma_kernel(
 }
 
 // ---------------------------------------------------------------------------------------------
-// dK, dV (key-stationary over the CSR transpose): grid = B*Hh*cpx*8, one wave per key cube
-// (cond_T == 0, so key cube j = noise cube j).  K and V rows of the key cube are B operands held
+// dK, dV (key-stationary over the CSR transpose): grid = B*Hh*(ccx+ncx)*8, one wave per key cube
+// (condition cubes, read from the cache and written to the cache gradients, and noise cubes).
+// K and V rows of the key cube are B operands held
 // in registers; per 32-query half of each query cube that selected j, the Q and dO rows are staged
 // straight into LDS (double buffered), S = Q K^T and dP = dO V^T read them as A operands, and
 // P, dS built in place in the accumulators are the B operands of dV^T += dO^T P and
@@ -250,8 +251,9 @@ __global__ __launch_bounds__(64) void bwd_dkdv_mfma_kernel(
     Geom g, const bf16_t* __restrict__ k_row, const bf16_t* __restrict__ v_row,
     const bf16_t* __restrict__ q_row, const bf16_t* __restrict__ do_row,
     const float2* __restrict__ ld_c, const int32_t* __restrict__ csr_off,
-    const int32_t* __restrict__ csr_list, float scale, float c_log2, int cpx,
-    float* __restrict__ dk, float* __restrict__ dv) {
+    const int32_t* __restrict__ csr_list, float scale, float c_log2, int ccx, int ncx,
+    float* __restrict__ dk, float* __restrict__ dv, float* __restrict__ dk_cache,
+    float* __restrict__ dv_cache) {
   constexpr int S = D / 16;
   constexpr int DB = D / 32;
   constexpr int cube_bytes = 64 * D * 2;
@@ -263,9 +265,16 @@ __global__ __launch_bounds__(64) void bwd_dkdv_mfma_kernel(
   const int L = blockIdx.x;
   const int xcd = L & 7;
   const int k8 = L >> 3;
-  const int bh = k8 / cpx;
-  const int j = xcd * cpx + (k8 % cpx);
-  if (j >= g.nbq) return;
+  // XCD x takes the x-th run of ccx condition cube ids and the x-th run of ncx noise cube ids
+  // of every (b, h), condition cubes (whose lists hold every query cube) first, so the XCDs
+  // carry equal work and the long items start early.
+  const int per = ccx + ncx;
+  const int bh = k8 / per;
+  const int m = k8 % per;
+  const bool cube_ok = m < ccx ? xcd * ccx + m < g.nbc : xcd * ncx + (m - ccx) < g.nbq;
+  if (!cube_ok) return;
+  // key cube id: condition cubes first, then noise cubes
+  const int j = m < ccx ? xcd * ccx + m : g.nbc + xcd * ncx + (m - ccx);
   const int b = bh / g.Hh, h = bh % g.Hh;
   const int lane = threadIdx.x;
   const int l32 = lane & 31;
@@ -292,9 +301,11 @@ __global__ __launch_bounds__(64) void bwd_dkdv_mfma_kernel(
   };
   if (nsteps > 0) stage_step(csr_list[beg], 0, st0);
 
-  // K and V rows of this key cube as B operands (lane = key, 8 consecutive d).
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(k_row + bh * bh_elems, bh_bytes);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(v_row + bh * bh_elems, bh_bytes);
+  // K and V rows of this key cube as B operands (lane = key, 8 consecutive d); the K/V gathers
+  // hold every key cube (condition cubes from the cache first).
+  const size_t kv_elems = (size_t)g.nbk * 64 * D;
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(k_row + bh * kv_elems, (size_t)g.nbk * cube_bytes);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(v_row + bh * kv_elems, (size_t)g.nbk * cube_bytes);
   bf16x8 kreg[2][S], vreg[2][S];
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
@@ -367,10 +378,14 @@ __global__ __launch_bounds__(64) void bwd_dkdv_mfma_kernel(
   }
   __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the last re-staging has landed
 
+  const bool cond = j < g.nbc;  // condition key cube: its gradients go to the cache tensors
+  float* dk_out = cond ? dk_cache : dk;
+  float* dv_out = cond ? dv_cache : dv;
+  const int jc = cond ? j : j - g.nbc;  // cube index inside its segment
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
-    const int tk = cube_token(g, j, 32 * kb + l32);
-    const size_t off = bnhd_offset(g, g.Nq, b, tk, h);
+    const int tk = cube_token(g, jc, 32 * kb + l32);
+    const size_t off = bnhd_offset(g, cond ? g.Nc : g.Nq, b, tk, h);
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -378,10 +393,10 @@ __global__ __launch_bounds__(64) void bwd_dkdv_mfma_kernel(
         const int d = 32 * db + 8 * r4 + 4 * hh;
         const f32x16& ak = acck[db][kb];
         const f32x16& av = accv[db][kb];
-        *reinterpret_cast<float4*>(dk + off + d) =
+        *reinterpret_cast<float4*>(dk_out + off + d) =
             make_float4(ak[4 * r4] * scale, ak[4 * r4 + 1] * scale, ak[4 * r4 + 2] * scale,
                         ak[4 * r4 + 3] * scale);
-        *reinterpret_cast<float4*>(dv + off + d) =
+        *reinterpret_cast<float4*>(dv_out + off + d) =
             make_float4(av[4 * r4], av[4 * r4 + 1], av[4 * r4 + 2], av[4 * r4 + 3]);
       }
   }
@@ -406,16 +421,19 @@ hipError_t launch_bwd_dq_mfma(const Geom& g, const bf16_t* q_row, const bf16_t* 
 hipError_t launch_bwd_dkdv_mfma(const Geom& g, const bf16_t* k_row, const bf16_t* v_row,
                                 const bf16_t* q_row, const bf16_t* do_row, const float2* ld_c,
                                 const int32_t* csr_off, const int32_t* csr_list, float scale,
-                                float* dk, float* dv, hipStream_t s) {
-  const int cpx = (g.nbq + 7) / 8;
-  dim3 grid((unsigned)(g.B * g.Hh * cpx * 8));
+                                float* dk, float* dv, float* dk_cache, float* dv_cache,
+                                hipStream_t s) {
+  const int ccx = (g.nbc + 7) / 8, ncx = (g.nbq + 7) / 8;
+  dim3 grid((unsigned)(g.B * g.Hh * (ccx + ncx) * 8));
   const float c_log2 = scale * kLog2e;
   if (g.D == 64)
     hipLaunchKernelGGL(bwd_dkdv_mfma_kernel<64>, grid, dim3(64), 0, s, g, k_row, v_row, q_row,
-                       do_row, ld_c, csr_off, csr_list, scale, c_log2, cpx, dk, dv);
+                       do_row, ld_c, csr_off, csr_list, scale, c_log2, ccx, ncx, dk, dv,
+                       dk_cache, dv_cache);
   else
     hipLaunchKernelGGL(bwd_dkdv_mfma_kernel<128>, grid, dim3(64), 0, s, g, k_row, v_row, q_row,
-                       do_row, ld_c, csr_off, csr_list, scale, c_log2, cpx, dk, dv);
+                       do_row, ld_c, csr_off, csr_list, scale, c_log2, ccx, ncx, dk, dv,
+                       dk_cache, dv_cache);
   return hipGetLastError();
 }
 
