@@ -80,7 +80,8 @@ class Problem:
         return self.cond_T * self.H * self.W
 
     def cubes_in(self, frames: int) -> int:
-        return (frames // self.cube_t) * (self.H // self.cube_h) * (self.W // self.cube_w)
+        # reading: partial edge cubes along H and W (ragged latent grids) count as cubes
+        return (frames // self.cube_t) * (-(-self.H // self.cube_h)) * (-(-self.W // self.cube_w))
 
     @property
     def nbq(self) -> int:
@@ -104,8 +105,8 @@ def check_problem(p: Problem) -> None:
         raise ProblemError("invalid", "cond_T must be >= 0")
     if p.cond_T >= p.T:
         raise ProblemError("shape", "cond_T must be < T")
-    if p.noise_T % p.cube_t or p.H % p.cube_h or p.W % p.cube_w or p.cond_T % p.cube_t:
-        raise ProblemError("shape", "grid not divisible by the cube")
+    if p.noise_T % p.cube_t or p.cond_T % p.cube_t:
+        raise ProblemError("shape", "frame counts not divisible by the cube")
 
 
 def num_selected(p: Problem, r: int) -> int:
@@ -115,30 +116,34 @@ def num_selected(p: Problem, r: int) -> int:
 
 # --------------------------------------------------------------------------------------------
 # Step 1: cube partition (reading: raster order over cube coordinates, t slowest, then h, then w;
-# inside a cube, raster order over (dt, dh, dw)).
+# inside a cube, raster order over (dt, dh, dw)).  Reading for ragged latent grids (H or W not a
+# multiple of the cube side, e.g. the 45-token height of 720p): the last cube row / column keeps
+# only the tokens of its box that lie inside the grid.
 # --------------------------------------------------------------------------------------------
 @lru_cache(maxsize=16)
 def _segment_cube_tokens_cached(frames, H, W, ct, ch, cw):
-    nt, nh, nw = frames // ct, H // ch, W // cw
-    out = np.empty((nt * nh * nw, ct * ch * cw), dtype=np.int64)
+    nt, nh, nw = frames // ct, -(-H // ch), -(-W // cw)
+    out = []
     for a in range(nt):
         for b in range(nh):
             for e in range(nw):
-                cube = (a * nh + b) * nw + e
-                slot = 0
+                members = []
                 for dt in range(ct):
                     for dh in range(ch):
                         for dw in range(cw):
                             t, h, w = a * ct + dt, b * ch + dh, e * cw + dw
-                            out[cube, slot] = (t * H + h) * W + w
-                            slot += 1
-    out.setflags(write=False)
-    return out
+                            if h < H and w < W:
+                                members.append((t * H + h) * W + w)
+                arr = np.array(members, dtype=np.int64)
+                arr.setflags(write=False)
+                out.append(arr)
+    return tuple(out)
 
 
-def segment_cube_tokens(p: Problem, frames: int) -> np.ndarray:
-    """[n_cubes, c] int64: the token indices (raster order inside a segment of `frames` frames)
-    belonging to each cube of that segment."""
+def segment_cube_tokens(p: Problem, frames: int) -> tuple:
+    """Per cube of a segment of `frames` frames, the int64 array of its token indices (raster
+    order inside the segment), cube by cube in raster cube order; every array has c entries
+    unless the cube sits on a ragged edge."""
     return _segment_cube_tokens_cached(frames, p.H, p.W, p.cube_t, p.cube_h, p.cube_w)
 
 
@@ -163,8 +168,8 @@ def block_pool(x: np.ndarray, p: Problem) -> np.ndarray:
     assert N == p.Nq and Hh == p.heads and D == p.head_dim
     out = np.empty((B, Hh, p.nbq, D), dtype=np.float64)
     for i in range(p.nbq):
-        members = np.asarray(x[:, toks[i], :, :], dtype=np.float64)  # [B, c, Hh, D]
-        out[:, :, i, :] = members.sum(axis=1) / p.c
+        members = np.asarray(x[:, toks[i], :, :], dtype=np.float64)  # [B, c_i, Hh, D]
+        out[:, :, i, :] = members.sum(axis=1) / len(toks[i])
     return out
 
 
@@ -300,8 +305,8 @@ def attn_bwd(q, k, v, dO, idx, p: Problem, scale: float, rows=None, key_cubes=No
     if cached and (k_cache is None or v_cache is None):
         raise ProblemError("invalid", "condition frames need k_cache and v_cache")
     qt = noise_cube_tokens(p)
-    ct_ = cond_cube_tokens(p) if cached else None
-    c, D = p.c, p.head_dim
+    ct_ = cond_cube_tokens(p) if cached else ()
+    D = p.head_dim
     full = rows is None and key_cubes is None
     want_rows = None if rows is None else set(map(tuple, rows))
     want_cols = None if key_cubes is None else set(map(tuple, key_cubes))
@@ -314,8 +319,10 @@ def attn_bwd(q, k, v, dO, idx, p: Problem, scale: float, rows=None, key_cubes=No
     else:
         dQ, dK, dV = {}, {}, {}
         for key in want_cols or ():
-            dK[key] = np.zeros((c, D))
-            dV[key] = np.zeros((c, D))
+            j = key[2]
+            n = len(ct_[j]) if j < p.nbc else len(qt[j - p.nbc])
+            dK[key] = np.zeros((n, D))
+            dV[key] = np.zeros((n, D))
     for b in range(p.batch):
         for h in range(p.heads):
             for i in range(p.nbq):
@@ -338,25 +345,28 @@ def attn_bwd(q, k, v, dO, idx, p: Problem, scale: float, rows=None, key_cubes=No
                 delta = np.sum(dOi * Oi, axis=1, keepdims=True)
                 dP = dOi @ Vs.T
                 dS = P * (dP - delta)
-                dKs = scale * (dS.T @ Qi)                   # [k_sel*c, D]
+                dKs = scale * (dS.T @ Qi)                   # [keys, D], cube after cube
                 dVs = P.T @ dOi
+                ends = np.cumsum([len(ct_[int(j)] if int(j) < p.nbc else qt[int(j) - p.nbc])
+                                  for j in sel])
+                starts = np.concatenate([[0], ends[:-1]])
                 if full:
                     dQ[b, qt[i], h, :] += scale * (dS @ Ks)
                     for pos, j in enumerate(sel):
                         j = int(j)
                         if j < p.nbc:
-                            dKc[b, ct_[j], h, :] += dKs[pos * c:(pos + 1) * c]
-                            dVc[b, ct_[j], h, :] += dVs[pos * c:(pos + 1) * c]
+                            dKc[b, ct_[j], h, :] += dKs[starts[pos]:ends[pos]]
+                            dVc[b, ct_[j], h, :] += dVs[starts[pos]:ends[pos]]
                         else:
-                            dK[b, qt[j - p.nbc], h, :] += dKs[pos * c:(pos + 1) * c]
-                            dV[b, qt[j - p.nbc], h, :] += dVs[pos * c:(pos + 1) * c]
+                            dK[b, qt[j - p.nbc], h, :] += dKs[starts[pos]:ends[pos]]
+                            dV[b, qt[j - p.nbc], h, :] += dVs[starts[pos]:ends[pos]]
                 else:
                     if need_q:
                         dQ[(b, h, i)] = scale * (dS @ Ks)
                     for pos in cols_here:
                         key = (b, h, int(sel[pos]))
-                        dK[key] += dKs[pos * c:(pos + 1) * c]
-                        dV[key] += dVs[pos * c:(pos + 1) * c]
+                        dK[key] += dKs[starts[pos]:ends[pos]]
+                        dV[key] += dVs[starts[pos]:ends[pos]]
     if not cached:
         return dQ, dK, dV
     if full:
@@ -398,8 +408,8 @@ def full_block_causal_fwd(q_full, k_full, v_full, p: Problem, r: int, r_cond: in
     check_problem(p)
     nbc, nbq = p.nbc, p.nbq
     ctok = cond_cube_tokens(p)
-    ntok = noise_cube_tokens(p) + p.Nc
-    all_tok = np.concatenate([ctok, ntok], axis=0) if nbc else ntok
+    ntok = [t + p.Nc for t in noise_cube_tokens(p)]
+    all_tok = list(ctok) + ntok
     B, N, Hh, D = q_full.shape
     O = np.full((B, N, Hh, D), np.nan)
     LSE = np.full((B, Hh, N), np.nan)

@@ -211,3 +211,40 @@ def test_cache_gradient_invariants():
     np.testing.assert_allclose(gk.sum(axis=1) + gkc.sum(axis=1), 0.0, atol=1e-12)
     # every noise query attends every condition cube, so every cache row gets gradient
     assert np.all(np.abs(gvc).sum(axis=-1) > 0)
+
+
+def test_ragged_grid_finite_differences_and_autograd():
+    """Partial edge cubes: central differences and torch autograd under the token mask."""
+    p = orc.Problem(1, 1, 64, 4, 6, 7, 2, 4, 4, 2)
+    rng = np.random.default_rng(31)
+    sn, sc = (1, p.Nq, 1, 64), (1, p.Nc, 1, 64)
+    x = {"q": rng.standard_normal(sn), "k": rng.standard_normal(sn), "v": rng.standard_normal(sn),
+         "k_cache": rng.standard_normal(sc), "v_cache": rng.standard_normal(sc)}
+    dO = rng.standard_normal(sn)
+    idx, _ = orc.select_topr(orc.block_pool(x["q"], p), orc.block_pool(x["k"], p), p, 1)
+    scale = 1 / math.sqrt(p.head_dim)
+    grads = dict(zip(("q", "k", "v", "k_cache", "v_cache"),
+                     orc.attn_bwd(x["q"], x["k"], x["v"], dO, idx, p, scale,
+                                  k_cache=x["k_cache"], v_cache=x["v_cache"])))
+    h = 1e-5
+    for name in grads:
+        for _ in range(6):
+            d = rng.standard_normal(x[name].shape)
+            xp = dict(x); xp[name] = x[name] + h * d
+            xm = dict(x); xm[name] = x[name] - h * d
+            fd = (_loss_cached(xp, dO, idx, p, scale) - _loss_cached(xm, dO, idx, p, scale)) / (2 * h)
+            an = float(np.sum(grads[name] * d))
+            assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (name, fd, an)
+    qt, ct = orc.noise_cube_tokens(p), orc.cond_cube_tokens(p)
+    mask = np.zeros((p.Nq, p.Nc + p.Nq), dtype=bool)
+    for i in range(p.nbq):
+        for j in idx[0, 0, i]:
+            j = int(j)
+            mask[np.ix_(qt[i], ct[j] if j < p.nbc else p.Nc + qt[j - p.nbc])] = True
+    rq, rk, rv = _autograd_ref(x["q"], np.concatenate([x["k_cache"], x["k"]], 1),
+                               np.concatenate([x["v_cache"], x["v"]], 1), dO, scale, mask)
+    np.testing.assert_allclose(grads["q"], rq, atol=1e-12)
+    np.testing.assert_allclose(grads["k_cache"], rk[:, :p.Nc], atol=1e-12)
+    np.testing.assert_allclose(grads["k"], rk[:, p.Nc:], atol=1e-12)
+    np.testing.assert_allclose(grads["v_cache"], rv[:, :p.Nc], atol=1e-12)
+    np.testing.assert_allclose(grads["v"], rv[:, p.Nc:], atol=1e-12)

@@ -133,8 +133,8 @@ def test_block_causal_cached_mode_equals_full_sequence():
             assert list(idx[b, h, g - p.nbc]) == s
     # the full-sequence result against torch SDPA with the token-level block-causal mask
     ctok = orc.cond_cube_tokens(p)
-    ntok = orc.noise_cube_tokens(p) + p.Nc
-    all_tok = np.concatenate([ctok, ntok])
+    ntok = [t + p.Nc for t in orc.noise_cube_tokens(p)]
+    all_tok = list(ctok) + ntok
     for b in range(2):
         for h in range(2):
             M = np.zeros((N, N), dtype=bool)
@@ -145,3 +145,24 @@ def test_block_causal_cached_mode_equals_full_sequence():
             ref = _sdpa(qf[b:b + 1, :, h:h + 1], kf[b:b + 1, :, h:h + 1], vf[b:b + 1, :, h:h + 1],
                         scale, M)
             np.testing.assert_allclose(Of[b:b + 1, :, h:h + 1], ref, atol=1e-12)
+
+
+@pytest.mark.parametrize("r", [0, 2, 5])
+def test_ragged_grid_matches_torch_sdpa_with_token_mask(r):
+    """Partial edge cubes (H = 9, W = 6 with 4x4 cube faces): the oracle's cube-level attention
+    equals dense SDPA under the token mask of the selection, and LSE is the masked logsumexp."""
+    p = orc.Problem(1, 2, 64, 4, 9, 6, 2, 4, 4, 0)
+    rng = np.random.default_rng(21)
+    x = {n: rng.standard_normal((1, p.Nq, 2, 64)) for n in ("q", "k", "v")}
+    scale = 1 / math.sqrt(p.head_dim)
+    qm, km = orc.block_pool(x["q"], p), orc.block_pool(x["k"], p)
+    idx, _ = orc.select_topr(qm, km, p, r)
+    O, LSE = orc.sparse_attn_fwd(x["q"], x["k"], x["v"], None, None, idx, p, scale)
+    for h in range(2):
+        M = _token_mask(p, idx[0, h])
+        sl = slice(h, h + 1)
+        ref = _sdpa(x["q"][:, :, sl], x["k"][:, :, sl], x["v"][:, :, sl], scale, M)
+        np.testing.assert_allclose(O[:, :, sl], ref, atol=1e-12, rtol=0)
+        s = scale * x["q"][0, :, h] @ x["k"][0, :, h].T
+        s[~M] = -np.inf
+        np.testing.assert_allclose(LSE[0, h], scipy.special.logsumexp(s, axis=1), atol=1e-12)

@@ -29,7 +29,7 @@ def test_partition_is_raster_cube_order(shape):
     for frames in (p.noise_T, p.cond_T):
         if frames == 0:
             continue
-        toks = orc.segment_cube_tokens(p, frames)
+        toks = np.stack(orc.segment_cube_tokens(p, frames))   # divisible grids: all cubes full
         nt, nh, nw = frames // p.cube_t, p.H // p.cube_h, p.W // p.cube_w
         assert toks.shape == (nt * nh * nw, p.c)
         # every token exactly once
@@ -93,7 +93,6 @@ def test_pool_constant_and_linear():
 
 @pytest.mark.parametrize("bad, kind", [
     (dict(T=5), "shape"),             # noise frames not divisible by cube_t
-    (dict(W=10), "shape"),
     (dict(cond_T=1, T=5), "shape"),   # cond_T not a cube multiple
     (dict(cond_T=4), "shape"),        # cond_T == T
     (dict(heads=0), "invalid"),
@@ -114,3 +113,77 @@ def test_scores_are_scaled_matmul():
     S = orc.block_scores(qm, km, 16)
     ref = np.einsum("bhid,bhjd->bhij", qm, km) * 0.25
     np.testing.assert_allclose(S, ref, rtol=1e-14, atol=1e-14)
+
+
+# ---------------------------------------------------------------------------------------------
+# Ragged latent grids: partial edge cubes along H and W.
+# ---------------------------------------------------------------------------------------------
+RAGGED = [
+    # T, H, W, ct, ch, cw, cond_T
+    (4, 9, 8, 2, 4, 4, 0),       # one partial cube row of height 1
+    (4, 6, 7, 2, 4, 4, 2),       # partial row and column, condition frames
+    (8, 45, 10, 4, 4, 4, 4),     # the 720p-class height 45
+    (2, 5, 5, 1, 2, 2, 0),
+]
+
+
+def test_ragged_grid_is_accepted():
+    p = orc.Problem(1, 1, 64, 4, 8, 10, 2, 4, 4, 0)
+    orc.check_problem(p)
+    assert p.nbq == 2 * 2 * 3
+
+
+@pytest.mark.parametrize("shape", RAGGED)
+def test_ragged_partition(shape):
+    p = _problem(shape)
+    for frames in (p.noise_T, p.cond_T):
+        if frames == 0:
+            continue
+        toks = orc.segment_cube_tokens(p, frames)
+        gh, gw = -(-p.H // p.cube_h), -(-p.W // p.cube_w)
+        assert len(toks) == frames // p.cube_t * gh * gw
+        flat = np.concatenate(toks)
+        assert np.array_equal(np.sort(flat), np.arange(frames * p.H * p.W))   # exactly once
+        # the cube of every token, from its coordinates alone
+        t, h, w = np.unravel_index(np.arange(frames * p.H * p.W), (frames, p.H, p.W))
+        cube_of = (t // p.cube_t * gh + h // p.cube_h) * gw + w // p.cube_w
+        for i, members in enumerate(toks):
+            assert np.all(cube_of[members] == i)
+            assert np.all(np.diff(members) > 0)
+            b, e = (i // gw) % gh, i % gw
+            assert len(members) == p.cube_t * min(p.cube_h, p.H - b * p.cube_h) * \
+                min(p.cube_w, p.W - e * p.cube_w)
+
+
+@pytest.mark.parametrize("shape", RAGGED)
+def test_ragged_pool_is_clipped_box_centre(shape):
+    p = _problem(shape, D=4)
+    t, h, w = np.unravel_index(np.arange(p.Nq), (p.noise_T, p.H, p.W))
+    x = np.stack([t, h, w, np.ones_like(t)], axis=-1).astype(np.float64)[None, :, None, :]
+    x = np.repeat(x, p.heads, axis=2)
+    pooled = orc.block_pool(x, p)
+    gh, gw = -(-p.H // p.cube_h), -(-p.W // p.cube_w)
+    for i in range(p.nbq):
+        a, b, e = i // (gh * gw), (i // gw) % gh, i % gw
+        he = min(p.cube_h, p.H - b * p.cube_h)
+        we = min(p.cube_w, p.W - e * p.cube_w)
+        np.testing.assert_allclose(pooled[0, :, i, :],
+                                   np.array([[a * p.cube_t + (p.cube_t - 1) / 2,
+                                              b * p.cube_h + (he - 1) / 2,
+                                              e * p.cube_w + (we - 1) / 2, 1.0]] * p.heads),
+                                   rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("shape", RAGGED)
+def test_ragged_pool_integer_inputs_exact(shape):
+    p = _problem(shape, B=2, Hh=3, D=5)
+    rng = np.random.default_rng(8)
+    x = rng.integers(-256, 257, size=(p.batch, p.Nq, p.heads, p.head_dim))
+    t, h, w = np.unravel_index(np.arange(p.Nq), (p.noise_T, p.H, p.W))
+    gh, gw = -(-p.H // p.cube_h), -(-p.W // p.cube_w)
+    cube_of = (t // p.cube_t * gh + h // p.cube_h) * gw + w // p.cube_w
+    sums = np.zeros((p.batch, p.nbq, p.heads, p.head_dim), dtype=np.int64)
+    np.add.at(sums, (slice(None), cube_of), x)
+    counts = np.bincount(cube_of, minlength=p.nbq)
+    expect = np.transpose(sums, (0, 2, 1, 3)) / counts[None, None, :, None]
+    np.testing.assert_array_equal(orc.block_pool(x.astype(np.float32), p), expect)
