@@ -108,6 +108,8 @@ def main() -> int:
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-continuation", action="store_true",
                     help="skip the continuation-mode forward measurement")
+    ap.add_argument("--no-ragged", action="store_true",
+                    help="skip the ragged 24x45x80 (real 720p latent) fwd+bwd measurement")
     ap.add_argument("--no-prologue", action="store_true",
                     help="skip the fused QK-norm + 3D RoPE prologue measurement")
     ap.add_argument("--no-dense", action="store_true",
@@ -239,6 +241,8 @@ def main() -> int:
         out["dense_vs_bsa_fwd"] = bench_dense(bsa, synth, torch, dev, t)
     if not args.no_prologue:
         out["qk_prologue"] = bench_prologue(bsa, torch, dev, p)
+    if not args.no_ragged:
+        out["real_latent_720p"] = bench_ragged(bsa, synth, torch, dev, args)
 
     if args.calib_copy_mib:
         n = args.calib_copy_mib * (1 << 20) // 4
@@ -351,6 +355,47 @@ def _time_fwd(bsa, torch, p, t, r, reps=3):
     tot = [sum(ms for _, ms in ev.elapsed_all()) for ev in evs]
     del ws, idx
     return ks, float(np.median(tot))
+
+
+def bench_ragged(bsa, synth, torch, dev, args, reps=3):
+    """One fwd+bwd step on the real 720p latent grid 24 x 45 x 80 (the last cube row is 1 token
+    high: partial edge cubes), same heads, cube and top-r as the headline workload."""
+    import numpy as np
+    w = synth.workload(3, H=45, W=80)
+    p = bsa.Problem(**w.shape_dict)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(4545)
+    shp = (p.batch, p.Nq, p.heads, p.head_dim)
+    t = {n: torch.randn(shp, generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+         for n in ("q", "k", "v", "dO")}
+    ks = bsa.bsa_num_selected(p, w.r)
+    scale = 1.0 / math.sqrt(p.head_dim)
+    wsf = torch.empty(bsa.bsa_workspace_bytes(p, torch.bfloat16, ks, False), dtype=torch.uint8,
+                      device=dev)
+    wsb = torch.empty(bsa.bsa_workspace_bytes(p, torch.bfloat16, ks, True), dtype=torch.uint8,
+                      device=dev)
+
+    def step():
+        qm = bsa.bsa_block_pool(p, t["q"])
+        km = bsa.bsa_block_pool(p, t["k"])
+        idx, _ = bsa.bsa_select_topr(p, qm, km, w.r, with_mask=False)
+        o, lse = bsa.bsa_sparse_attn_fwd(p, t["q"], t["k"], t["v"], idx, ks, scale, workspace=wsf)
+        bsa.bsa_sparse_attn_bwd(p, t["q"], t["k"], t["v"], o, t["dO"], lse, idx, ks, scale,
+                                workspace=wsb)
+
+    step()
+    torch.cuda.synchronize()
+    ms = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        step()
+        e1.record()
+        e1.synchronize()
+        ms.append(e0.elapsed_time(e1))
+    return {"grid": "24x45x80 (45 = 11 full cube rows + 1 row of height 1)", "k_sel": ks,
+            "step_ms": round(float(np.median(ms)), 3),
+            "note": "pool x2, select, fwd, bwd; partial edge cubes masked in the kernels"}
 
 
 def bench_prologue(bsa, torch, dev, p, reps=5):

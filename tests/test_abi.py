@@ -48,6 +48,7 @@ def test_num_selected_and_workspace(L):
     assert L.bsa_num_selected(ctypes.byref(_p(T=8, cond_T=4)), 0) == 4 + 1
     assert L.bsa_num_selected(ctypes.byref(_p()), -1) == -1
     assert L.bsa_num_selected(ctypes.byref(_p(T=7)), 1) == -1
+    assert L.bsa_num_selected(ctypes.byref(_p(W=10)), 100) == 2 * 2 * 3       # ragged: 3 along w
     big = bsa.Problem(1, 32, 128, 24, 48, 80, 4, 4, 4)
     assert bsa.bsa_num_selected(big, 144) == 145
     import torch
@@ -66,7 +67,9 @@ def test_num_selected_and_workspace(L):
 
 
 @pytest.mark.parametrize("kw, status", [
-    (dict(T=7), SHAPE), (dict(W=10), SHAPE), (dict(cond_T=2), SHAPE), (dict(cond_T=8), SHAPE),
+    # (a W or H that is not a cube multiple is a valid ragged grid, so it is not listed here:
+    # these calls carry placeholder pointers and must fail validation before any launch)
+    (dict(T=7), SHAPE), (dict(cond_T=2), SHAPE), (dict(cond_T=8), SHAPE),
     (dict(head_dim=96), UNSUPPORTED), (dict(cube_t=8, cube_h=8, cube_w=8, T=8, H=8, W=8),
                                        UNSUPPORTED),
     (dict(heads=0), INVALID), (dict(cond_T=-4), INVALID),

@@ -63,12 +63,17 @@ class Problem:
         return self.cond_T * self.H * self.W
 
     @property
+    def _cubes_hw(self) -> int:
+        # partial edge cubes on a ragged grid count as cubes
+        return (-(-self.H // self.cube_h)) * (-(-self.W // self.cube_w))
+
+    @property
     def nbq(self) -> int:
-        return (self.T - self.cond_T) // self.cube_t * (self.H // self.cube_h) * (self.W // self.cube_w)
+        return (self.T - self.cond_T) // self.cube_t * self._cubes_hw
 
     @property
     def nbc(self) -> int:
-        return self.cond_T // self.cube_t * (self.H // self.cube_h) * (self.W // self.cube_w)
+        return self.cond_T // self.cube_t * self._cubes_hw
 
     @property
     def nbk(self) -> int:

@@ -57,9 +57,8 @@ bsa_status_t check_problem(const bsa_problem_t* p, Geom* g) {
     return fail(BSA_ERR_INVALID_ARG, "every size must be positive");
   if (p->cond_T < 0) return fail(BSA_ERR_INVALID_ARG, "cond_T must be >= 0");
   if (p->cond_T >= p->T) return fail(BSA_ERR_SHAPE, "cond_T must be < T");
-  if ((p->T - p->cond_T) % p->cube_t || p->H % p->cube_h || p->W % p->cube_w ||
-      p->cond_T % p->cube_t)
-    return fail(BSA_ERR_SHAPE, "grid (noise frames, H, W, cond_T) not divisible by the cube");
+  if ((p->T - p->cond_T) % p->cube_t || p->cond_T % p->cube_t)
+    return fail(BSA_ERR_SHAPE, "noise frames and cond_T must be multiples of cube_t");
   if (p->head_dim != 64 && p->head_dim != 128)
     return fail(BSA_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
   const long long c = (long long)p->cube_t * p->cube_h * p->cube_w;

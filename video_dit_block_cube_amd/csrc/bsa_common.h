@@ -3,8 +3,9 @@
 // Cube partition of the latent grid (tokens grouped into small 3D cubes: "LongCat-Video :
 // Generate 1 minute long AI videos with this model", Data Science in Your Pocket, section
 // "Sparse attention"): cubes are numbered in raster order over cube coordinates (t slowest, then
-// h, then w) inside each segment (condition frames, noise frames); the c tokens of a cube are
-// visited in raster order over (dt, dh, dw).
+// h, then w) inside each segment (condition frames, noise frames); the c slots of a cube are
+// visited in raster order over (dt, dh, dw).  On a ragged grid (H or W not a multiple of the cube
+// side) the last cube row / column is partial: its slots outside the grid hold no token.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -24,6 +25,7 @@ struct Geom {
   int gh, gw;    // cubes along h, w
   int gtq, gtc;  // cubes along t in the noise / condition segment
   int nbq, nbc, nbk;
+  int ragged;    // H % ch or W % cw non-zero: partial edge cubes exist
 };
 
 inline Geom make_geom(int B, int Hh, int D, int T, int H, int W, int ct, int ch, int cw,
@@ -35,8 +37,9 @@ inline Geom make_geom(int B, int Hh, int D, int T, int H, int W, int ct, int ch,
   g.nT = T - condT;
   g.Nq = g.nT * H * W;
   g.Nc = condT * H * W;
-  g.gh = H / ch;
-  g.gw = W / cw;
+  g.gh = (H + ch - 1) / ch;
+  g.gw = (W + cw - 1) / cw;
+  g.ragged = (H % ch) != 0 || (W % cw) != 0;
   g.gtq = g.nT / ct;
   g.gtc = condT / ct;
   g.nbq = g.gtq * g.gh * g.gw;
@@ -55,7 +58,37 @@ __host__ __device__ inline int cube_token(const Geom& g, int cube, int slot) {
   const int r2 = slot / g.cw;
   const int dh = r2 % g.ch;
   const int dt = r2 / g.ch;
-  return ((a * g.ct + dt) * g.H + bb * g.ch + dh) * g.W + e * g.cw + dw;
+  const int hh = bb * g.ch + dh, ww = e * g.cw + dw;
+  if (hh >= g.H || ww >= g.W) return -1;  // slot of a partial edge cube outside the grid
+  return ((a * g.ct + dt) * g.H + hh) * g.W + ww;
+}
+
+// Extent of cube `cube` of a segment along h and w (ch, cw except on a ragged edge).
+__host__ __device__ inline void cube_extent(const Geom& g, int cube, int& he, int& we) {
+  const int e = cube % g.gw, bb = (cube / g.gw) % g.gh;
+  he = g.H - bb * g.ch < g.ch ? g.H - bb * g.ch : g.ch;
+  we = g.W - e * g.cw < g.cw ? g.W - e * g.cw : g.cw;
+}
+
+// Number of tokens of cube `cube` of a segment.
+__host__ __device__ inline int cube_count(const Geom& g, int cube) {
+  int he, we;
+  cube_extent(g, cube, he, we);
+  return g.ct * he * we;
+}
+
+// Bit k set iff slot 32*half + k of the cube holds a token (all bits off the ragged edge).
+__device__ inline uint32_t cube_half_mask(const Geom& g, int cube, int half) {
+  int he, we;
+  cube_extent(g, cube, he, we);
+  if (he == g.ch && we == g.cw) return 0xffffffffu;
+  uint32_t m = 0u;
+  for (int k = 0; k < 32; ++k) {
+    const int s = 32 * half + k;
+    const int dw = s % g.cw, dh = (s / g.cw) % g.ch;
+    if (s < g.c && dh < he && dw < we) m |= 1u << k;
+  }
+  return m;
 }
 
 // Element offset of (b, token, head, 0) in a [B, N, Hh, D] tensor.

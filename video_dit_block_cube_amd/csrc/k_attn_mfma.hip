@@ -90,9 +90,11 @@ __device__ __forceinline__ bf16x8 pack8(const f32x16& a, int base) {
 // Online-softmax attention of one 64-token query cube over the 32-key half cubes
 // [t_begin, t_end) of its (ascending) selection row, where row position p stands for entry
 // p + (p >= p_split ? p_skip : 0) (two disjoint spans walked as one; p_skip = 0 for one span).
-// Accumulates O^T (unnormalised), the running base-2 max and this lane's partial row sums.
-template <int D, bool EARLY_K>
-__device__ __forceinline__ void attend_span(const bf16x8* __restrict__ qs,
+// Accumulates O^T (unnormalised), the running base-2 max and this lane's partial row sums.  On a
+// ragged grid (RAGGED, a separate instantiation so divisible grids carry none of its registers),
+// key slots of a partial edge cube that hold no token get S = -inf.
+template <int D, bool EARLY_K, bool RAGGED>
+__device__ __forceinline__ void attend_span(const Geom& g, const bf16x8* __restrict__ qs,
                                             __amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv,
                                             const int32_t* __restrict__ irow, int t_begin,
                                             int t_end, int p_split, int p_skip, float c_log2,
@@ -102,11 +104,12 @@ __device__ __forceinline__ void attend_span(const bf16x8* __restrict__ qs,
   constexpr int DB = D / 32;
   constexpr int cube_bytes = 64 * D * 2;
   const int vlane = lane * 16;
+  int cur_j;  // key cube id of tile t
   bf16x8 kr[S], vr[DB * 2];
   {
     const int p0 = t_begin >> 1;
-    const int off0 =
-        irow[p0 + (p0 >= p_split ? p_skip : 0)] * cube_bytes + (t_begin & 1) * (32 * D * 2);
+    cur_j = irow[p0 + (p0 >= p_split ? p_skip : 0)];
+    const int off0 = cur_j * cube_bytes + (t_begin & 1) * (32 * D * 2);
 #pragma unroll
     for (int s = 0; s < S; ++s) kr[s] = bld16(rk, vlane, off0 + s * 1024);
 #pragma unroll
@@ -129,9 +132,24 @@ __device__ __forceinline__ void attend_span(const bf16x8* __restrict__ qs,
       st[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr[s], q0, st[0], 0, 0, 0);
       st[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr[s], q1, st[1], 0, 0, 0);
     }
+    if constexpr (RAGGED) {
+      // accumulator row 8*(e/4) + 4*(lane/32) + e%4 of S^T is key slot 32*(t&1) + that row
+      const uint32_t km = cube_half_mask(g, cur_j < g.nbc ? cur_j : cur_j - g.nbc, t & 1);
+      if (km != 0xffffffffu) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int krow = 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+          if (!((km >> krow) & 1u)) {
+            st[0][e] = -INFINITY;
+            st[1][e] = -INFINITY;
+          }
+        }
+      }
+    }
     const int tn = t + 1 < t_end ? t + 1 : t;
     const int pn = tn >> 1;
-    const int noff = irow[pn + (pn >= p_split ? p_skip : 0)] * cube_bytes + (tn & 1) * (32 * D * 2);
+    const int nxt_j = irow[pn + (pn >= p_split ? p_skip : 0)];
+    const int noff = nxt_j * cube_bytes + (tn & 1) * (32 * D * 2);
     if constexpr (EARLY_K) {
       // ---- request next tile's K now (longer lead, more live registers) ----
 #pragma unroll
@@ -192,6 +210,7 @@ __device__ __forceinline__ void attend_span(const bf16x8* __restrict__ qs,
     }
 #pragma unroll
     for (int u = 0; u < DB * 2; ++u) vr[u] = bld16(rv, vlane, noff + u * 1024);
+    cur_j = nxt_j;
   }
 }
 
@@ -206,7 +225,7 @@ __device__ __forceinline__ void zero_acc(f32x16 (&acc)[D / 32][2]) {
 }
 
 // Single pass: one wave per query cube over its whole selection; writes O (bf16) and LSE.
-template <int D, bool EARLY_K>
+template <int D, bool EARLY_K, bool RAGGED>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_mfma_kernel(
     Geom g, const bf16_t* __restrict__ q_row, const bf16_t* __restrict__ krow,
     const bf16_t* __restrict__ vtr, const int32_t* __restrict__ idx, int k_sel, float c_log2,
@@ -234,13 +253,14 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   zero_acc<D>(acc);
   float m_run[2] = {-INFINITY, -INFINITY};
   float l_part[2] = {0.f, 0.f};
-  attend_span<D, EARLY_K>(qs, rk, rv, irow, 0, 2 * k_sel, k_sel, 0, c_log2, lane, acc, m_run,
+  attend_span<D, EARLY_K, RAGGED>(g, qs, rk, rv, irow, 0, 2 * k_sel, k_sel, 0, c_log2, lane, acc, m_run,
                           l_part);
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     const float l = l_part[qb] + __shfl_xor(l_part[qb], 32, 64);
     const float inv = 1.0f / l;
     const int tq = cube_token(g, i, 32 * qb + l32);
+    if (tq < 0) continue;  // slot outside a ragged grid
     bf16_t* orow = o + bnhd_offset(g, g.Nq, b, tq, h);
 #pragma unroll
     for (int db = 0; db < DB; ++db)
@@ -264,7 +284,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 // [64][D] row-major) plus its base-2 max and row sum.  Range s runs on XCD s%8, whose L2 then
 // only ever holds that range of the head's K/V; the XCD takes its ranges one after the other
 // (s = xcd, xcd + 8, ...), heads in order within each.
-template <int D, bool EARLY_K>
+template <int D, bool EARLY_K, bool RAGGED>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_split_kernel(
     Geom g, const bf16_t* __restrict__ q_row, const bf16_t* __restrict__ krow,
     const bf16_t* __restrict__ vtr, const int32_t* __restrict__ idx, int k_sel, float c_log2,
@@ -310,7 +330,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   zero_acc<D>(acc);
   float m_run[2] = {-INFINITY, -INFINITY};
   float l_part[2] = {0.f, 0.f};
-  attend_span<D, EARLY_K>(qs, rk, rv, irow, 2 * lo1, 2 * (lo1 + n_sel), hi1, lo2 - hi1, c_log2,
+  attend_span<D, EARLY_K, RAGGED>(g, qs, rk, rv, irow, 2 * lo1, 2 * (lo1 + n_sel), hi1, lo2 - hi1, c_log2,
                           lane, acc, m_run, l_part);
   bf16_t* op = o_part + item * (64 * D);
 #pragma unroll
@@ -377,6 +397,7 @@ __global__ __launch_bounds__(256) void fwd_merge_kernel(Geom g, int ns,
   }
   const float inv = 1.0f / Lsum;
   const int tok = cube_token(g, i, row);
+  if (tok < 0) return;  // slot outside a ragged grid
   bf16_t* orow = o + bnhd_offset(g, g.Nq, b, tok, h) + part * DQ;
 #pragma unroll
   for (int c8 = 0; c8 < DQ / 8; ++c8) {
@@ -407,7 +428,7 @@ int fwd_split_ranges(const Geom& g, int k_sel, int requested) {
   return (head_kv > 8.0 * (1 << 20) && mostly_noise) ? 8 : 1;
 }
 
-template <int D, bool EK>
+template <int D, bool EK, bool RG>
 static hipError_t launch_fwd_t(const Geom& g, const bf16_t* q_row, const bf16_t* k_row,
                                const bf16_t* v_trans, const int32_t* idx, int k_sel,
                                float c_log2, void* o, float* lse, int ns, void* split_ws,
@@ -415,7 +436,7 @@ static hipError_t launch_fwd_t(const Geom& g, const bf16_t* q_row, const bf16_t*
   if (ns <= 1) {
     const int cpx = (g.nbq + 7) / 8;
     dim3 grid((unsigned)(g.B * g.Hh * cpx * 8));
-    hipLaunchKernelGGL((fwd_mfma_kernel<D, EK>), grid, dim3(64), 0, s, g, q_row,
+    hipLaunchKernelGGL((fwd_mfma_kernel<D, EK, RG>), grid, dim3(64), 0, s, g, q_row,
                        k_row, v_trans, idx, k_sel, c_log2, cpx, (bf16_t*)o, lse);
     return hipGetLastError();
   }
@@ -426,7 +447,7 @@ static hipError_t launch_fwd_t(const Geom& g, const bf16_t* q_row, const bf16_t*
   float2* ml_part = reinterpret_cast<float2*>(o_part + items * 64 * g.D);
   const int passes = (ns + 7) / 8;
   dim3 grid((unsigned)(8 * passes * g.B * g.Hh * g.nbq));
-  hipLaunchKernelGGL((fwd_split_kernel<D, EK>), grid, dim3(64), 0, s, g, q_row,
+  hipLaunchKernelGGL((fwd_split_kernel<D, EK, RG>), grid, dim3(64), 0, s, g, q_row,
                      k_row, v_trans, idx, k_sel, c_log2, ns, rcc, rcn, o_part, ml_part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -445,15 +466,18 @@ hipError_t launch_fwd_mfma(const Geom& g, const bf16_t* q_row, const bf16_t* k_r
   // BSA_FWD_EARLY_K=0/1).
   const char* env = std::getenv("BSA_FWD_EARLY_K");
   const bool early = env ? std::atoi(env) != 0 : g.D == 64;
+#define BSA_FWD_CALL(DD, EK)                                                                   \
+  (g.ragged ? launch_fwd_t<DD, EK, true>(g, q_row, k_row, v_trans, idx, k_sel, c_log2, o, lse, \
+                                         ns, split_ws, s)                                        \
+            : launch_fwd_t<DD, EK, false>(g, q_row, k_row, v_trans, idx, k_sel, c_log2, o, lse, \
+                                          ns, split_ws, s))
+  hipError_t e;
   if (g.D == 64)
-    return early ? launch_fwd_t<64, true>(g, q_row, k_row, v_trans, idx, k_sel, c_log2, o, lse, ns,
-                                          split_ws, s)
-                 : launch_fwd_t<64, false>(g, q_row, k_row, v_trans, idx, k_sel, c_log2, o, lse, ns,
-                                           split_ws, s);
-  return early ? launch_fwd_t<128, true>(g, q_row, k_row, v_trans, idx, k_sel, c_log2, o, lse, ns,
-                                         split_ws, s)
-               : launch_fwd_t<128, false>(g, q_row, k_row, v_trans, idx, k_sel, c_log2, o, lse, ns,
-                                          split_ws, s);
+    e = early ? BSA_FWD_CALL(64, true) : BSA_FWD_CALL(64, false);
+  else
+    e = early ? BSA_FWD_CALL(128, true) : BSA_FWD_CALL(128, false);
+#undef BSA_FWD_CALL
+  return e;
 }
 
 }  // namespace bsa

@@ -25,6 +25,11 @@ __device__ __forceinline__ void load_row_f32(const T* __restrict__ src, float* _
   for (int d = lane4; d < D; d += 4) dst[d] = load_as_f32<T>(src + d);
 }
 
+// Token of slot `slot` of a cube, or -1 past the cube or outside a ragged grid.
+__device__ __forceinline__ int slot_token(const Geom& g, int cube, int slot) {
+  return slot < g.c ? cube_token(g, cube, slot) : -1;
+}
+
 __device__ __forceinline__ float group4_max(float v) {
   v = fmaxf(v, __shfl_xor(v, 1, 64));
   v = fmaxf(v, __shfl_xor(v, 2, 64));
@@ -71,6 +76,7 @@ __global__ __launch_bounds__(256) void fwd_simt_kernel(Geom g, const T* __restri
   float* Ks = Qs + kTile * LD;
   float* Vs = Ks + kTile * LD;
   float* Ps = Vs + kTile * LD;  // [64][65]
+  float* kok = Ps + kTile * 65;  // 1 where the tile's key slot holds a token
   const int nqc = (g.c + kTile - 1) / kTile;
   const int i = blockIdx.x / nqc;
   const int qc0 = (blockIdx.x % nqc) * kTile;
@@ -79,11 +85,12 @@ __global__ __launch_bounds__(256) void fwd_simt_kernel(Geom g, const T* __restri
   const int tid = threadIdx.x;
   const int row = tid >> 2, sub = tid & 3;
   const int qrow = qc0 + row;
-  const bool row_ok = qrow < g.c;
+  const int qtok = slot_token(g, i, qrow);
+  const bool row_ok = qtok >= 0;
 
   {
     float* dst = Qs + row * LD;
-    if (row_ok) load_row_f32(q + bnhd_offset(g, g.Nq, b, cube_token(g, i, qrow), h), dst, D, sub);
+    if (row_ok) load_row_f32(q + bnhd_offset(g, g.Nq, b, qtok, h), dst, D, sub);
     else for (int d = sub; d < D; d += 4) dst[d] = 0.f;
   }
   constexpr int DO = D / 4;
@@ -103,16 +110,17 @@ __global__ __launch_bounds__(256) void fwd_simt_kernel(Geom g, const T* __restri
     for (int kc0 = 0; kc0 < g.c; kc0 += kTile) {
       __syncthreads();
       {
-        const int key = kc0 + row;
+        const int ktok = slot_token(g, cube, kc0 + row);
         float* kd = Ks + row * LD;
         float* vd = Vs + row * LD;
-        if (key < g.c) {
-          const size_t off = bnhd_offset(g, N, b, cube_token(g, cube, key), h);
+        if (ktok >= 0) {
+          const size_t off = bnhd_offset(g, N, b, ktok, h);
           load_row_f32(ksrc + off, kd, D, sub);
           load_row_f32(vsrc + off, vd, D, sub);
         } else {
           for (int d = sub; d < D; d += 4) { kd[d] = 0.f; vd[d] = 0.f; }
         }
+        if (sub == 0) kok[row] = ktok >= 0 ? 1.f : 0.f;
       }
       __syncthreads();
       float s[16];
@@ -120,16 +128,17 @@ __global__ __launch_bounds__(256) void fwd_simt_kernel(Geom g, const T* __restri
 #pragma unroll
       for (int m = 0; m < 16; ++m) {
         const int key = sub + 4 * m;
-        s[m] = (kc0 + key < g.c) ? dot_lds<D>(Qs + row * LD, Ks + key * LD) * scale : -INFINITY;
+        s[m] = kok[key] != 0.f ? dot_lds<D>(Qs + row * LD, Ks + key * LD) * scale : -INFINITY;
         mt = fmaxf(mt, s[m]);
       }
       mt = group4_max(mt);
       const float m_new = fmaxf(m_run, mt);
-      const float alpha = expf(m_run - m_new);
+      // a tile with no key yet seen keeps m at -inf: nothing to rescale (avoids -inf - -inf)
+      const float alpha = m_new == -INFINITY ? 1.f : expf(m_run - m_new);
       float psum = 0.f;
 #pragma unroll
       for (int m = 0; m < 16; ++m) {
-        const float p = expf(s[m] - m_new);
+        const float p = s[m] == -INFINITY ? 0.f : expf(s[m] - m_new);
         psum += p;
         Ps[row * 65 + sub + 4 * m] = p;
       }
@@ -148,7 +157,7 @@ __global__ __launch_bounds__(256) void fwd_simt_kernel(Geom g, const T* __restri
   }
   const float l = group4_sum(l_part);
   if (row_ok) {
-    const int tok = cube_token(g, i, qrow);
+    const int tok = qtok;
     T* orow = o + bnhd_offset(g, g.Nq, b, tok, h) + sub * DO;
     const float inv = 1.0f / l;
 #pragma unroll
@@ -177,6 +186,7 @@ __global__ __launch_bounds__(256) void bwd_dq_simt_kernel(Geom g, const T* __res
   float* Ks = dOs + kTile * LD;
   float* Vs = Ks + kTile * LD;
   float* Ps = Vs + kTile * LD;  // [64][65]
+  float* kok = Ps + kTile * 65;  // 1 where the tile's key slot holds a token
   const int nqc = (g.c + kTile - 1) / kTile;
   const int i = blockIdx.x / nqc;
   const int qc0 = (blockIdx.x % nqc) * kTile;
@@ -185,13 +195,14 @@ __global__ __launch_bounds__(256) void bwd_dq_simt_kernel(Geom g, const T* __res
   const int tid = threadIdx.x;
   const int row = tid >> 2, sub = tid & 3;
   const int qrow = qc0 + row;
-  const bool row_ok = qrow < g.c;
+  const int qtok = slot_token(g, i, qrow);
+  const bool row_ok = qtok >= 0;
   float lse_r = 0.f, dl_r = 0.f;
   {
     float* dq_ = Qs + row * LD;
     float* dd = dOs + row * LD;
     if (row_ok) {
-      const size_t off = bnhd_offset(g, g.Nq, b, cube_token(g, i, qrow), h);
+      const size_t off = bnhd_offset(g, g.Nq, b, qtok, h);
       load_row_f32(q + off, dq_, D, sub);
       load_row_f32(d_o + off, dd, D, sub);
       lse_r = lse_c[((size_t)bh * g.nbq + i) * g.c + qrow];
@@ -210,23 +221,24 @@ __global__ __launch_bounds__(256) void bwd_dq_simt_kernel(Geom g, const T* __res
     for (int kc0 = 0; kc0 < g.c; kc0 += kTile) {
       __syncthreads();
       {
-        const int key = kc0 + row;
+        const int ktok = slot_token(g, cube, kc0 + row);
         float* kd = Ks + row * LD;
         float* vd = Vs + row * LD;
-        if (key < g.c) {
-          const size_t off = bnhd_offset(g, g.Nq, b, cube_token(g, cube, key), h);
+        if (ktok >= 0) {
+          const size_t off = bnhd_offset(g, g.Nq, b, ktok, h);
           load_row_f32(k + off, kd, D, sub);
           load_row_f32(v + off, vd, D, sub);
         } else {
           for (int d = sub; d < D; d += 4) { kd[d] = 0.f; vd[d] = 0.f; }
         }
+        if (sub == 0) kok[row] = ktok >= 0 ? 1.f : 0.f;
       }
       __syncthreads();
 #pragma unroll
       for (int m = 0; m < 16; ++m) {
         const int key = sub + 4 * m;
         float ds = 0.f;
-        if (row_ok && kc0 + key < g.c) {
+        if (row_ok && kok[key] != 0.f) {
           const float s = dot_lds<D>(Qs + row * LD, Ks + key * LD) * scale;
           const float p = expf(s - lse_r);
           const float dp = dot_lds<D>(dOs + row * LD, Vs + key * LD);
@@ -244,7 +256,7 @@ __global__ __launch_bounds__(256) void bwd_dq_simt_kernel(Geom g, const T* __res
     }
   }
   if (row_ok) {
-    float* out = dq + bnhd_offset(g, g.Nq, b, cube_token(g, i, qrow), h) + sub * DO;
+    float* out = dq + bnhd_offset(g, g.Nq, b, qtok, h) + sub * DO;
 #pragma unroll
     for (int e = 0; e < DO; ++e) out[e] = acc[e] * scale;
   }
@@ -277,12 +289,13 @@ __global__ __launch_bounds__(256) void bwd_dkdv_simt_kernel(
   const int tid = threadIdx.x;
   const int row = tid >> 2, sub = tid & 3;  // row = key within the tile
   const int key = kc0 + row;
-  const bool key_ok = key < g.c;
+  const int ktok = slot_token(g, j, key);
+  const bool key_ok = ktok >= 0;
   {
     float* kd = Ks + row * LD;
     float* vd = Vs + row * LD;
     if (key_ok) {
-      const size_t off = bnhd_offset(g, g.Nq, b, cube_token(g, j, key), h);
+      const size_t off = bnhd_offset(g, g.Nq, b, ktok, h);
       load_row_f32(k + off, kd, D, sub);
       load_row_f32(v + off, vd, D, sub);
     } else {
@@ -302,10 +315,12 @@ __global__ __launch_bounds__(256) void bwd_dkdv_simt_kernel(
       __syncthreads();
       {
         const int qrow = qc0 + row;
+        const int qtok = slot_token(g, i, qrow);
         float* qd = Qs + row * LD;
         float* dd = dOs + row * LD;
-        if (qrow < g.c) {
-          const size_t off = bnhd_offset(g, g.Nq, b, cube_token(g, i, qrow), h);
+        // a slot without a token has LSE = +inf (from the delta pass): its P row is 0
+        if (qtok >= 0) {
+          const size_t off = bnhd_offset(g, g.Nq, b, qtok, h);
           load_row_f32(q + off, qd, D, sub);
           load_row_f32(d_o + off, dd, D, sub);
           if (sub == 0) {
@@ -314,7 +329,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_simt_kernel(
           }
         } else {
           for (int d = sub; d < D; d += 4) { qd[d] = 0.f; dd[d] = 0.f; }
-          if (sub == 0) { lse_s[row] = 0.f; dl_s[row] = 0.f; }
+          if (sub == 0) { lse_s[row] = INFINITY; dl_s[row] = 0.f; }
         }
       }
       __syncthreads();
@@ -352,7 +367,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_simt_kernel(
     }
   }
   if (key_ok) {
-    const size_t off = bnhd_offset(g, g.Nq, b, cube_token(g, j, key), h) + sub * DO;
+    const size_t off = bnhd_offset(g, g.Nq, b, ktok, h) + sub * DO;
 #pragma unroll
     for (int e = 0; e < DO; ++e) {
       dk[off + e] = acc_k[e] * scale;
@@ -375,7 +390,7 @@ hipError_t launch_fwd_simt(const Geom& g, bool bf16, const void* q, const void* 
                            float scale, void* o, float* lse, hipStream_t s) {
   const int nqc = (g.c + kTile - 1) / kTile;
   dim3 grid(g.nbq * nqc, g.B * g.Hh);
-  const size_t lds = simt_lds(g.D, 3, false);
+  const size_t lds = simt_lds(g.D, 3, true);  // stats region holds the key flags
 #define BSA_FWD(T, DD)                                                                        \
   do {                                                                                         \
     auto kern = fwd_simt_kernel<T, DD>;                                                        \
@@ -398,7 +413,7 @@ hipError_t launch_bwd_dq_simt(const Geom& g, bool bf16, const void* q, const voi
                               float* dq, hipStream_t s) {
   const int nqc = (g.c + kTile - 1) / kTile;
   dim3 grid(g.nbq * nqc, g.B * g.Hh);
-  const size_t lds = simt_lds(g.D, 4, false);
+  const size_t lds = simt_lds(g.D, 4, true);  // stats region holds the key flags
 #define BSA_DQ(T, DD)                                                                          \
   do {                                                                                          \
     auto kern = bwd_dq_simt_kernel<T, DD>;                                                      \

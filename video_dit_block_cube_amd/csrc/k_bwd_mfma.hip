@@ -103,7 +103,7 @@ __device__ __forceinline__ void stage_half(__amdgpu_buffer_rsrc_t r, int soff, l
 // (held in registers) as B operands; dS^T stays in the accumulator registers and, as bf16, is
 // the B operand of dQ^T += K^T dS^T, whose A operand is read transposed from the staged K rows.
 // ---------------------------------------------------------------------------------------------
-template <int D>
+template <int D, bool RAGGED>
 __global__ __launch_bounds__(64) void bwd_dq_mfma_kernel(
     Geom g, const bf16_t* __restrict__ q_row, const bf16_t* __restrict__ do_row,
     const bf16_t* __restrict__ k_row, const bf16_t* __restrict__ v_row,
@@ -191,6 +191,11 @@ __global__ __launch_bounds__(64) void bwd_dq_mfma_kernel(
       dpt[0] = mfma32(ka[s], dreg[0][s], dpt[0]);
       dpt[1] = mfma32(ka[s], dreg[1][s], dpt[1]);
     }
+    // Ragged grids need no key mask here: a key slot without a token has a zero K row in the
+    // gather, so its dS adds nothing to dQ = dS K as long as it is finite.  Its P = exp(-LSE)
+    // could overflow for a very negative LSE, so the ragged instantiation clamps P at 1 (a valid
+    // P is <= 1; the clamp only trims rounding).  A query slot without a token has LSE = +inf,
+    // so its P row is 0.
     bf16x8 kt[DB * 2];
 #pragma unroll
     for (int db = 0; db < DB; ++db)
@@ -204,7 +209,8 @@ __global__ __launch_bounds__(64) void bwd_dq_mfma_kernel(
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int r = 8 * s2 + e;
-          const float p = fast_exp2(fmaf(st[qb][r], c_log2, -lse2[qb]));
+          float p = fast_exp2(fmaf(st[qb][r], c_log2, -lse2[qb]));
+          if constexpr (RAGGED) p = fminf(p, 1.0f);
           dsb[s2][qb][e] = (__bf16)(p * (dpt[qb][r] - dl[qb]));
         }
 #pragma unroll
@@ -224,6 +230,7 @@ __global__ __launch_bounds__(64) void bwd_dq_mfma_kernel(
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     const int tq = cube_token(g, i, 32 * qb + l32);
+    if (tq < 0) continue;  // slot outside a ragged grid
     float* out = dq + bnhd_offset(g, g.Nq, b, tq, h);
 #pragma unroll
     for (int db = 0; db < DB; ++db)
@@ -385,6 +392,7 @@ __global__ __launch_bounds__(64) void bwd_dkdv_mfma_kernel(
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
     const int tk = cube_token(g, jc, 32 * kb + l32);
+    if (tk < 0) continue;  // slot outside a ragged grid
     const size_t off = bnhd_offset(g, cond ? g.Nc : g.Nq, b, tk, h);
 #pragma unroll
     for (int db = 0; db < DB; ++db)
@@ -409,12 +417,15 @@ hipError_t launch_bwd_dq_mfma(const Geom& g, const bf16_t* q_row, const bf16_t* 
   const int cpx = (g.nbq + 7) / 8;
   dim3 grid((unsigned)(g.B * g.Hh * cpx * 8));
   const float c_log2 = scale * kLog2e;
-  if (g.D == 64)
-    hipLaunchKernelGGL(bwd_dq_mfma_kernel<64>, grid, dim3(64), 0, s, g, q_row, do_row, k_row,
-                       v_row, ld_c, idx, k_sel, scale, c_log2, cpx, dq);
-  else
-    hipLaunchKernelGGL(bwd_dq_mfma_kernel<128>, grid, dim3(64), 0, s, g, q_row, do_row, k_row,
-                       v_row, ld_c, idx, k_sel, scale, c_log2, cpx, dq);
+#define BSA_DQ(DD, RG)                                                                          \
+  hipLaunchKernelGGL((bwd_dq_mfma_kernel<DD, RG>), grid, dim3(64), 0, s, g, q_row, do_row, k_row, \
+                     v_row, ld_c, idx, k_sel, scale, c_log2, cpx, dq)
+  if (g.D == 64) {
+    if (g.ragged) BSA_DQ(64, true); else BSA_DQ(64, false);
+  } else {
+    if (g.ragged) BSA_DQ(128, true); else BSA_DQ(128, false);
+  }
+#undef BSA_DQ
   return hipGetLastError();
 }
 

@@ -35,9 +35,8 @@ __global__ __launch_bounds__(64) void delta_kernel(Geom g, const T* __restrict__
   for (int s0 = 0; s0 < g.c; s0 += rpi) {
     const int s = s0 + rr;
     float acc = 0.f;
-    int tok = 0;
-    if (s < g.c) {
-      tok = cube_token(g, i, s);
+    const int tok = s < g.c ? cube_token(g, i, s) : -1;
+    if (tok >= 0) {
       const size_t off = bnhd_offset(g, g.Nq, b, tok, h) + (size_t)sub * V;
       const uint4 a = *reinterpret_cast<const uint4*>(o + off);
       const uint4 c2 = *reinterpret_cast<const uint4*>(d_o + off);
@@ -49,7 +48,8 @@ __global__ __launch_bounds__(64) void delta_kernel(Geom g, const T* __restrict__
     for (int off = lpr >> 1; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
     if (s < g.c && sub == 0) {
       const size_t dst = ((size_t)bh * g.nbq + i) * g.c + s;
-      const float lv = lse[(size_t)bh * g.Nq + tok];
+      // a slot outside a ragged grid gets LSE = +inf: P = exp(S - LSE) = 0 for that row
+      const float lv = tok >= 0 ? lse[(size_t)bh * g.Nq + tok] : INFINITY;
       delta_c[dst] = acc;
       lse_c[dst] = lv;
       if (ld_c) ld_c[dst] = make_float2(lv, acc);

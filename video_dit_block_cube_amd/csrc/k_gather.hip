@@ -46,8 +46,10 @@ __global__ __launch_bounds__(256) void gather_kernel(Geom g, const bf16_t* __res
   constexpr int CPR = D / 8;  // 16-byte chunks per token row
   for (int u = tid; u < UNITS; u += 256) {
     const int row = u / CPR, ch = u % CPR;
-    const size_t off = bnhd_offset(g, N, b, cube_token(g, cube, row), h) + ch * 8;
-    *reinterpret_cast<uint4*>(tile + row * LD + ch * 8) = *reinterpret_cast<const uint4*>(src + off);
+    const int tok = cube_token(g, cube, row);  // -1: slot outside a ragged grid -> zero row
+    *reinterpret_cast<uint4*>(tile + row * LD + ch * 8) =
+        tok >= 0 ? *reinterpret_cast<const uint4*>(src + bnhd_offset(g, N, b, tok, h) + ch * 8)
+                 : make_uint4(0u, 0u, 0u, 0u);
   }
   __syncthreads();
   const size_t blk = (((size_t)b * g.Hh + h) * g.nbk + j) * (size_t)(64 * D);

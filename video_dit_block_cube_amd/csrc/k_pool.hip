@@ -39,7 +39,7 @@ __global__ __launch_bounds__(256) void pool_kernel(Geom g, const T* __restrict__
   const int tsplit = 256 / G;
   const int tg = tid / G;
   const int cg = tid % G;
-  const float cf = (float)g.c;
+  const float cf = (float)cube_count(g, cube);  // fewer than c on a ragged edge
 
   for (int ch0 = 0; ch0 < nchunks; ch0 += G) {
     const int ch = ch0 + cg;
@@ -51,6 +51,7 @@ __global__ __launch_bounds__(256) void pool_kernel(Geom g, const T* __restrict__
 #pragma unroll 4
       for (int s = tg; s < g.c; s += tsplit) {
         const int tok = cube_token(g, cube, s);
+        if (tok < 0) continue;  // slot outside a ragged grid
         const T* row = x + ((size_t)b * g.Nq + tok) * (size_t)cols + (size_t)ch * V;
         const uint4 raw = *reinterpret_cast<const uint4*>(row);
         const T* vals = reinterpret_cast<const T*>(&raw);

@@ -76,7 +76,7 @@ __global__ __launch_bounds__(256) void prologue_kernel(Geom g, int t_offset,
   const int lanes_per_head = g.D / V;  // 8 or 16 (bf16), 16 or 32 (fp32): inside one wave
   const int s6 = 2 * (g.D / 6);
   const int wt = g.D - 2 * s6;  // time block width; height and width blocks are s6 wide
-  const float inv_c = 1.0f / (float)g.c;
+  const float inv_c = 1.0f / (float)cube_count(g, cube);  // fewer than c on a ragged edge
   const double log2_theta = log2((double)theta);
   // cube origin on the grid and the rotation table of this cube
   const int tok0 = cube_token(g, cube, 0);
@@ -123,6 +123,7 @@ __global__ __launch_bounds__(256) void prologue_kernel(Geom g, int t_offset,
     // every lane of a head group runs the same token sequence, so the shuffles line up
     for (int s = tg; s < g.c; s += tsplit) {
       const int tok = cube_token(g, cube, s);
+      if (tok < 0) continue;  // slot outside a ragged grid (same for the whole head group)
       const size_t off = ((size_t)b * g.Nq + tok) * (size_t)cols + (size_t)e0;
       float v[V];
       {
