@@ -214,6 +214,8 @@ def main() -> int:
     for k, v in avg.items():
         kf = kernel_flops(k, p, ks)
         per_kernel[k] = {"avg_ms": round(v, 4),
+                         "median_ms": round(float(np.median(stage_ms[k])), 4),
+                         "p90_ms": round(float(np.percentile(stage_ms[k], 90)), 4),
                          **({"tflops": round(kf / (v * 1e-3) / 1e12, 1),
                              "frac_peak": round(kf / (v * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
                             if kf else {})}
@@ -226,8 +228,12 @@ def main() -> int:
                                "cube 4x4x4, top-r=144 + own cube, QKNorm q/k, dO~N(0,1)",
                    "k_sel": ks, "selected_fraction": round(ks / p.nbq, 4),
                    "fwd_tflop": round(f_fwd / 1e12, 3),
-                   "bwd_tflop_effective": round(2.5 * f_fwd / 1e12, 3)},
+                   "bwd_tflop_effective": round(2.5 * f_fwd / 1e12, 3),
+                   "bwd_tflop_4gemm": round(2.0 * f_fwd / 1e12, 3)},
         "pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "value_4gemm_bwd": round(f_fwd * 3.0 / (ms_per_step * 1e-3) / 1e12, 2),
+        "step_ms_median": round(float(np.median(step_ms)), 3),
+        "step_ms_p90": round(float(np.percentile(step_ms, 90)), 3),
         "fwd_ms": round(avg.get("gather_qkv", 0) + avg.get("attn_fwd_mfma", 0), 3),
         "bwd_ms": round(sum(avg.get(k, 0) for k in ("bwd_prep", "gather_qkv_do",
                                                       "bwd_dkdv_mfma", "bwd_dq_mfma")), 3),

@@ -65,8 +65,9 @@ typedef enum { BSA_F32 = 0, BSA_BF16 = 1 } bsa_dtype_t;
 /* Shape of one problem.  T counts all frames, condition frames included; cond_T = 0 means no
  * condition cache and plain (non-causal) block-sparse attention.
  * Requirements: all sizes > 0 except cond_T >= 0; head_dim in {64, 128}; T - cond_T and cond_T
- * divisible by cube_t, cond_T < T; cube size c = cube_t*cube_h*cube_w <= 256; per (b, h) at most
- * 40000 noise cubes.  H and W need not be multiples of cube_h, cube_w (ragged latent grids such
+ * divisible by cube_t, cond_T < T; cube size c = cube_t*cube_h*cube_w <= 256; at most 39808
+ * cubes per segment (the selection keeps one row of keys in LDS), and for the backward at most
+ * 39936 key cubes (condition + noise) in all.  H and W need not be multiples of cube_h, cube_w (ragged latent grids such
  * as the 45-token height of 720p): the last cube row / column then keeps only the tokens of its
  * box that lie inside the grid -- its mean divides by that count and its missing slots are
  * neither keys nor queries.  Cube counts are ceil(H/cube_h) * ceil(W/cube_w) per cube layer. */

@@ -157,3 +157,23 @@ def test_prologue_argument_errors(L):
     assert f(p, 1, 0, FAKE, None, one, ctypes.c_float(float("nan")), FAKE, FAKE, None) == INVALID
     assert f(p, 7, 0, FAKE, None, one, e, FAKE, FAKE, None) == INVALID        # dtype
     assert f(ctypes.byref(_p(T=7)), 1, 0, FAKE, None, one, e, FAKE, FAKE, None) == SHAPE
+
+
+def test_size_limits(L):
+    """Largest accepted problems (selection row in LDS; CSR transpose for the backward), checked
+    without launching: bsa_num_selected validates the problem, the backward fails its key-cube
+    check before any launch."""
+    at_limit = _p(heads=1, T=4, H=4 * 311, W=4 * 128)          # 311 * 128 = 39808 noise cubes
+    over = _p(heads=1, T=4, H=4 * 311, W=4 * 128 + 1)          # ragged: 311 * 129 cubes
+    assert L.bsa_num_selected(ctypes.byref(at_limit), 3) == 4
+    assert L.bsa_num_selected(ctypes.byref(over), 3) == -1
+    assert L.bsa_block_pool(ctypes.byref(over), 1, FAKE, FAKE, None) == UNSUPPORTED
+    # 39808 condition + 39808 noise key cubes: the forward is valid, the backward is not
+    pc = ctypes.byref(_p(heads=1, T=8, H=4 * 311, W=4 * 128, cond_T=4))
+    sc = ctypes.c_float(0.1)
+    ks = L.bsa_num_selected(pc, 1)
+    assert ks == 39808 + 1 + 1
+    assert L.bsa_sparse_attn_bwd(pc, 1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ks,
+                                 sc, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40,
+                                 None) == UNSUPPORTED
+    assert b"39936" in L.bsa_last_error()

@@ -27,7 +27,12 @@ thread_local int t_nstages = 0;
 thread_local int t_path = 0;
 
 constexpr size_t kAlign = 256;
-constexpr int kMaxNoiseCubes = 40000;
+// Cubes per segment: one selection row (a 4-byte key per noise cube), the query descriptor and a
+// 1024-entry histogram share the 160 KiB of LDS -- (nbq + D + 1024) * 4 <= 160 KiB at D = 128.
+constexpr int kMaxNoiseCubes = 39808;
+// Key cubes (condition + noise) for the backward: the CSR transpose scans nbk counters plus a
+// 1024-entry scan buffer in LDS -- (nbk + 1024) * 4 <= 160 KiB.
+constexpr int kMaxBwdKeyCubes = 39936;
 
 bsa_status_t fail(bsa_status_t st, const std::string& msg) {
   t_err = msg;
@@ -63,11 +68,12 @@ bsa_status_t check_problem(const bsa_problem_t* p, Geom* g) {
     return fail(BSA_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
   const long long c = (long long)p->cube_t * p->cube_h * p->cube_w;
   if (c > 256) return fail(BSA_ERR_UNSUPPORTED, "cube size must be <= 256 tokens");
-  const long long nbq = (long long)(p->T - p->cond_T) / p->cube_t * (p->H / p->cube_h) *
-                        (p->W / p->cube_w);
-  const long long nbc = (long long)p->cond_T / p->cube_t * (p->H / p->cube_h) * (p->W / p->cube_w);
+  const long long hw = (long long)((p->H + p->cube_h - 1) / p->cube_h) *
+                       ((p->W + p->cube_w - 1) / p->cube_w);  // partial edge cubes included
+  const long long nbq = (long long)(p->T - p->cond_T) / p->cube_t * hw;
+  const long long nbc = (long long)p->cond_T / p->cube_t * hw;
   if (nbq > kMaxNoiseCubes || nbc > kMaxNoiseCubes)
-    return fail(BSA_ERR_UNSUPPORTED, "at most 40000 cubes per segment");
+    return fail(BSA_ERR_UNSUPPORTED, "at most 39808 cubes per segment");
   const long long tokens = (long long)p->T * p->H * p->W;
   if (tokens * p->heads * p->head_dim * p->batch > (1LL << 40))
     return fail(BSA_ERR_UNSUPPORTED, "problem too large");
@@ -300,6 +306,8 @@ bsa_status_t bsa_sparse_attn_bwd(const bsa_problem_t* p, bsa_dtype_t dtype, cons
     if ((st = check_ksel(g, k_sel)) != BSA_OK) return st;
     if (!q || !k || !v || !o || !d_o || !lse || !idx || !dq || !dk || !dv)
       return fail(BSA_ERR_INVALID_ARG, "every tensor pointer must be non-NULL");
+    if (g.nbk > kMaxBwdKeyCubes)
+      return fail(BSA_ERR_UNSUPPORTED, "the backward supports at most 39936 key cubes");
     const bool cached = g.condT > 0;
     const bool any_cache = k_cache || v_cache || dk_cache || dv_cache;
     const bool all_cache = k_cache && v_cache && dk_cache && dv_cache;
