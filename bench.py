@@ -118,8 +118,9 @@ def main() -> int:
                     help="also run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the block sparse "
-              "attention path here is single-GPU, see DESIGN.md for how it would shard.",
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): the block sparse "
+              "attention path here runs on one GPU. Across GPUs it would shard by heads (one "
+              "all-to-all before and one after, Ulysses style); that path is not built.",
               file=sys.stderr)
         return 2
 

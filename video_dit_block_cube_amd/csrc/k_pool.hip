@@ -1,8 +1,8 @@
 // k_pool.hip -- per-cube mean pool of a [B, Nq, Hh, D] token tensor (HBM-bound).
 //
-// The cube descriptor is the mean of the cube's token vectors, per head (relevance between cubes
-// is judged by similarity, "LongCat-Video : Generate 1 minute long AI videos with this model",
-// Data Science in Your Pocket, section "Sparse attention").
+// The cube descriptor is the mean of the cube's token vectors, per head (which cubes matter to
+// each other is decided by similarity, "LongCat-Video : Generate 1 minute long AI videos with
+// this model", Data Science in Your Pocket, section "Sparse attention").
 //
 // MI355X design: one workgroup per (batch, cube) reads the cube's c token rows; a token row holds
 // every head (Hh*D contiguous elements, 8 KB for 32 heads x 128 bf16), so each 16-byte lane load
