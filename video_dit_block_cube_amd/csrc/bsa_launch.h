@@ -38,7 +38,7 @@ hipError_t launch_bwd_dkdv_simt(const Geom& g, bool bf16, const void* q, const v
                                 hipStream_t s);
 
 // k_bwd_prep.hip: Delta and LSE in cube order ([B, Hh, nbq, c]) and the CSR transpose of idx;
-// ld_c (may be NULL) additionally receives the interleaved (LSE, Delta) pairs.
+// ld_c (may be NULL) additionally receives the interleaved (LSE * log2(e), Delta) pairs.
 hipError_t launch_delta(const Geom& g, bool bf16, const void* o, const void* d_o,
                         const float* lse, float* delta_c, float* lse_c, float2* ld_c,
                         hipStream_t s);

@@ -157,7 +157,7 @@ __global__ __launch_bounds__(64) void bwd_dq_mfma_kernel(
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     const float2 ld = ld_c[((size_t)bh * g.nbq + i) * 64 + 32 * qb + l32];
-    lse2[qb] = ld.x * kLog2e;
+    lse2[qb] = ld.x;  // LSE in base 2
     dl[qb] = ld.y;
   }
 
@@ -265,7 +265,7 @@ __global__ __launch_bounds__(64) void bwd_dkdv_mfma_kernel(
   constexpr int DB = D / 32;
   constexpr int cube_bytes = 64 * D * 2;
   constexpr int half_bytes = 32 * D * 2;
-  constexpr int stage_bytes = 2 * half_bytes + 256;  // Q rows | dO rows | 32 (LSE, Delta) pairs
+  constexpr int stage_bytes = 2 * half_bytes + 256;  // Q rows | dO rows | 32 (LSE2, Delta) pairs
   __shared__ __attribute__((aligned(16))) char stage0[stage_bytes];
   __shared__ __attribute__((aligned(16))) char stage1[stage_bytes];
 
@@ -298,7 +298,8 @@ __global__ __launch_bounds__(64) void bwd_dkdv_mfma_kernel(
       make_rsrc(ld_c + (size_t)bh * g.nbq * 64, (size_t)g.nbq * 64 * sizeof(float2));
   lds_char* st0 = (lds_char*)stage0;
   lds_char* st1 = (lds_char*)stage1;
-  // one 32-query half of query cube i: Q rows, dO rows and the (LSE, Delta) pairs -> a stage
+  // one 32-query half of query cube i: Q rows, dO rows and the (base-2 LSE, Delta) pairs -> a
+  // stage
   auto stage_step = [&](int i, int qb, lds_char* dst) {
     stage_half<D>(rq, i * cube_bytes + qb * half_bytes, dst, lane);
     stage_half<D>(rd, i * cube_bytes + qb * half_bytes, dst + half_bytes, lane);
@@ -351,7 +352,7 @@ __global__ __launch_bounds__(64) void bwd_dkdv_mfma_kernel(
         dp = mfma32(lds_row_frag(cur + half_bytes, lane, s), vreg[kb][s], dp);
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
-        // pairs (lse, delta) of rows 8*r4 + 4*hh + 0..3
+        // pairs (base-2 lse, delta) of rows 8*r4 + 4*hh + 0..3
         const f32x4 p01 = ldp[(8 * r4 + 4 * hh) / 2];
         const f32x4 p23 = ldp[(8 * r4 + 4 * hh) / 2 + 1];
         const float lv[4] = {p01[0], p01[2], p23[0], p23[2]};
@@ -359,7 +360,7 @@ __global__ __launch_bounds__(64) void bwd_dkdv_mfma_kernel(
 #pragma unroll
         for (int e4 = 0; e4 < 4; ++e4) {
           const int r = 4 * r4 + e4;
-          const float p = fast_exp2(fmaf(st[r], c_log2, -lv[e4] * kLog2e));
+          const float p = fast_exp2(fmaf(st[r], c_log2, -lv[e4]));
           pb[kb][r >> 3][r & 7] = (__bf16)p;
           dsb[kb][r >> 3][r & 7] = (__bf16)(p * (dp[r] - dv4[e4]));
         }
@@ -378,10 +379,12 @@ __global__ __launch_bounds__(64) void bwd_dkdv_mfma_kernel(
         }
       }
   };
-  for (int t = 0; t < nsteps; ++t) {
-    lds_char* cur = (t & 1) ? st1 : st0;
-    lds_char* nxt = (t & 1) ? st0 : st1;
-    step(t, cur, nxt);
+  // nsteps is even (two 32-query halves per listed query cube); fixed stage roles per half let
+  // the compiler see that this step's LDS reads never alias the next step's LDS-bound loads,
+  // so it does not drain those loads before the transposed reads
+  for (int t = 0; t < nsteps; t += 2) {
+    step(t, st0, st1);
+    step(t + 1, st1, st0);
   }
   __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the last re-staging has landed
 

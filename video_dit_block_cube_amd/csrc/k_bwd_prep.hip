@@ -52,7 +52,7 @@ __global__ __launch_bounds__(64) void delta_kernel(Geom g, const T* __restrict__
       const float lv = tok >= 0 ? lse[(size_t)bh * g.Nq + tok] : INFINITY;
       delta_c[dst] = acc;
       lse_c[dst] = lv;
-      if (ld_c) ld_c[dst] = make_float2(lv, acc);
+      if (ld_c) ld_c[dst] = make_float2(lv * kLog2e, acc);  // base-2 LSE for exp2
     }
   }
 }
