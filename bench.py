@@ -58,10 +58,14 @@ def traffic_from_profile(stage: str):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
-    src = os.path.join(ROOT, kv.get("source", ""))
-    if not kv.get("source") or not os.path.exists(src):
+    # "source" lists the kernel's files (comma separated); the hash covers their bytes in order
+    srcs = [os.path.join(ROOT, f.strip()) for f in kv.get("source", "").split(",") if f.strip()]
+    if not srcs or not all(os.path.exists(f) for f in srcs):
         return None
-    if hashlib.sha256(open(src, "rb").read()).hexdigest() != kv.get("source_sha256"):
+    h = hashlib.sha256()
+    for f in srcs:
+        h.update(open(f, "rb").read())
+    if h.hexdigest() != kv.get("source_sha256"):
         return None
     try:
         return float(kv["hbm_bytes_per_launch"])

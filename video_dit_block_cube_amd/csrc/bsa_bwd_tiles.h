@@ -1,0 +1,86 @@
+// bsa_bwd_tiles.h -- tile helpers shared by the gfx950 backward kernels (dQ and dK/dV): buffer
+// loads, the bf16 MFMA step, and the LDS staging of ROW-layout half cubes with their plain and
+// transposed (ds_read_b64_tr_b16) operand reads.
+//
+// ROW gather layout (lane = token, 8 consecutive d per 16 bytes): a 32-row half block is D/16
+// steps of 1 KB, step s holding lane l's 16 bytes at (s*64 + l)*16.
+#pragma once
+
+#include "bsa_launch.h"
+
+namespace bsa {
+
+namespace {
+
+__device__ __forceinline__ bf16x8 ld16g(const bf16_t* p) {
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p));
+}
+__device__ __forceinline__ bf16x8 bld16(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, size_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ void zero16(f32x16& a) {
+#pragma unroll
+  for (int e = 0; e < 16; ++e) a[e] = 0.f;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------------------------
+// Shared LDS helpers.
+// ---------------------------------------------------------------------------------------------
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) char lds_char;
+
+// Operand fragment of a ROW-layout 32-row half block staged in LDS: lane's 16 bytes of step s.
+__device__ __forceinline__ bf16x8 lds_row_frag(const lds_char* stage, int lane, int s) {
+  return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(stage + (s * 64 + lane) * 16);
+}
+
+// Byte offset (inside a staged ROW half block) of lane's transposed read for operand (db, s2),
+// half eh: ds_read_b64_tr_b16 gives lane m of each 16-lane group g element k of
+// v[4k + m/4][m%4], where v[n] is the 4-element run at lane n's address.  Pointing lane n at
+// row 16*s2 + 8*eh + 4*(g/2) + n/4, columns d = 32*db + 16*(g%2) + 4*(n%4) .. +3 turns the run
+// into the TRANS operand (lane = d, 8 rows in accumulator-row order).
+__device__ __forceinline__ int tr_lane_base(int lane) {
+  const int g = lane >> 4, n = lane & 15;
+  // ROW element (row r, column d) sits at ((s'*64 + lane')*8 + e')*2 with lane' = (d/64)*32 + r,
+  // s' = (d%64)/8, e' = d%8; the lane-dependent part:
+  return ((128 * (g & 1) + 64 * ((n & 3) >> 1) + 4 * (g >> 1) + (n >> 2)) * 8 + 4 * (n & 1)) * 2;
+}
+// The row-split point of the ROW layout is d = D/2: column d lives at lane' = (d/(D/2))*32 + r,
+// step s' = (d%(D/2))/8.  With d = 32*db + (lane part), that gives per-(db, s2, eh) constants:
+template <int D>
+__device__ __forceinline__ int tr_const(int db, int s2, int eh) {
+  if constexpr (D == 128) return ((256 * (db & 1) + 32 * (db >> 1) + 16 * s2 + 8 * eh) * 8) * 2;
+  else return ((32 * db + 16 * s2 + 8 * eh) * 8) * 2;  // D == 64
+}
+template <int D>
+__device__ __forceinline__ bf16x8 lds_trans_frag(const lds_char* stage, int lane_base, int db,
+                                                 int s2) {
+  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4i16*)(stage + lane_base + tr_const<D>(db, s2, 0)));
+  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4i16*)(stage + lane_base + tr_const<D>(db, s2, 1)));
+  typedef short v8i16 __attribute__((ext_vector_type(8)));
+  const v8i16 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, both);
+}
+
+// One 32-row half block (S*1 KB) of a ROW-gathered tensor -> LDS, no VGPRs in between.
+template <int D>
+__device__ __forceinline__ void stage_half(__amdgpu_buffer_rsrc_t r, int soff, lds_char* dst,
+                                           int lane) {
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(dst + s * 1024),
+                                             16, lane * 16, soff + s * 1024, 0, 0);
+}
+
+}  // namespace bsa

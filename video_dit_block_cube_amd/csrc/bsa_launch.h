@@ -65,8 +65,9 @@ hipError_t launch_fwd_mfma(const Geom& g, const bf16_t* q_row, const bf16_t* k_r
                            const bf16_t* v_trans, const int32_t* idx, int k_sel, float scale,
                            void* o, float* lse, int ns, void* split_ws, hipStream_t s);
 
-// k_bwd_mfma.hip: bf16 MFMA backward kernels for c == 64, D in {64, 128}; every operand comes
-// from the ROW gather layout (transposed operands are read from LDS with ds_read_b64_tr_b16).
+// k_bwd_mfma.hip (dK/dV), k_bwd_dq.hip (dQ): bf16 MFMA backward kernels for c == 64, D in
+// {64, 128}; every operand comes from the ROW gather layout (transposed operands are read from
+// LDS with ds_read_b64_tr_b16).
 // k_row / v_row cover all nbk key cubes (condition cubes first), q_row / do_row the nbq query
 // cubes; dK/dV of condition key cubes go to dk_cache / dv_cache ([B, Nc, Hh, D]).
 hipError_t launch_bwd_dq_mfma(const Geom& g, const bf16_t* q_row, const bf16_t* do_row,

@@ -1,4 +1,4 @@
-// k_bwd_mfma.hip -- block-sparse attention backward on bf16 MFMA (gfx950), c == 64.
+// k_bwd_mfma.hip -- block-sparse attention backward, dK and dV, on bf16 MFMA (gfx950), c == 64.
 //
 // The backward ships alongside the forward for training ("LongCat-Video 高效長視頻生成探索世界
 // 模型的第壹步", meituan.com talk, section 2.2); the selection is a discrete choice and is held
@@ -6,243 +6,15 @@
 //   dV_j += P^T dO_i,  dS = P o (dO_i V_j^T - Delta_i),  dQ_i += scale*dS K_j,
 //   dK_j += scale*dS^T Q_i.
 //
-// MI355X design: two kernels, each owning its output in registers so no fp32 atomics are needed.
-// Every operand comes from the ROW gather layout (lane = token, 8 consecutive d per 16 bytes);
-// the streamed operand's rows are staged straight into LDS with buffer_load ... lds and its
-// transposed uses are read back with ds_read_b64_tr_b16, so each tile crosses the fabric once.
-//  * dQ (query-stationary, one wave = one 64-token query cube): Q and dO rows in registers; per
-//    32-key half cube, K and V rows staged in LDS; S^T = K Q^T and dP^T = V dO^T on MFMA, dS^T in
-//    place in the accumulators, converted to bf16, is the B operand of dQ^T += K^T dS^T.
-//  * dK/dV (key-stationary over the CSR transpose, one wave = one 64-token key cube): K and V
-//    rows in registers; per 32-query half of each query cube that selected this key cube, Q and
-//    dO rows staged in LDS; S = Q K^T and dP = dO V^T, then P and dS converted in place are the
-//    B operands of dV^T += dO^T P and dK^T += Q^T dS.
-//  The next tile is requested as soon as the current one is staged; per-lane byte offsets stay
-//  constant and the wave-uniform tile offset rides in an SGPR (buffer loads).
-#include "bsa_launch.h"
+// MI355X design: two kernels (dQ here and dK/dV), each owning its output in registers so no fp32
+// atomics are needed.  Every operand comes from the ROW gather layout; the streamed operand's
+// rows are staged straight into LDS with buffer_load ... lds and its transposed uses are read
+// back with ds_read_b64_tr_b16, so each tile crosses the fabric once.  The next tile is requested
+// as soon as the current one is staged; per-lane byte offsets stay constant and the wave-uniform
+// tile offset rides in an SGPR (buffer loads).
+#include "bsa_bwd_tiles.h"
 
 namespace bsa {
-
-namespace {
-
-__device__ __forceinline__ bf16x8 ld16g(const bf16_t* p) {
-  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p));
-}
-__device__ __forceinline__ bf16x8 bld16(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
-  return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
-}
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, size_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
-                                           0x00020000);
-}
-__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ void zero16(f32x16& a) {
-#pragma unroll
-  for (int e = 0; e < 16; ++e) a[e] = 0.f;
-}
-
-}  // namespace
-
-// ---------------------------------------------------------------------------------------------
-// Shared LDS helpers.
-// ---------------------------------------------------------------------------------------------
-typedef short v4i16 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) char lds_char;
-
-// Operand fragment of a ROW-layout 32-row half block staged in LDS: lane's 16 bytes of step s.
-__device__ __forceinline__ bf16x8 lds_row_frag(const lds_char* stage, int lane, int s) {
-  return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(stage + (s * 64 + lane) * 16);
-}
-
-// Byte offset (inside a staged ROW half block) of lane's transposed read for operand (db, s2),
-// half eh: ds_read_b64_tr_b16 gives lane m of each 16-lane group g element k of
-// v[4k + m/4][m%4], where v[n] is the 4-element run at lane n's address.  Pointing lane n at
-// row 16*s2 + 8*eh + 4*(g/2) + n/4, columns d = 32*db + 16*(g%2) + 4*(n%4) .. +3 turns the run
-// into the TRANS operand (lane = d, 8 rows in accumulator-row order).
-__device__ __forceinline__ int tr_lane_base(int lane) {
-  const int g = lane >> 4, n = lane & 15;
-  // ROW element (row r, column d) sits at ((s'*64 + lane')*8 + e')*2 with lane' = (d/64)*32 + r,
-  // s' = (d%64)/8, e' = d%8; the lane-dependent part:
-  return ((128 * (g & 1) + 64 * ((n & 3) >> 1) + 4 * (g >> 1) + (n >> 2)) * 8 + 4 * (n & 1)) * 2;
-}
-// The row-split point of the ROW layout is d = D/2: column d lives at lane' = (d/(D/2))*32 + r,
-// step s' = (d%(D/2))/8.  With d = 32*db + (lane part), that gives per-(db, s2, eh) constants:
-template <int D>
-__device__ __forceinline__ int tr_const(int db, int s2, int eh) {
-  if constexpr (D == 128) return ((256 * (db & 1) + 32 * (db >> 1) + 16 * s2 + 8 * eh) * 8) * 2;
-  else return ((32 * db + 16 * s2 + 8 * eh) * 8) * 2;  // D == 64
-}
-template <int D>
-__device__ __forceinline__ bf16x8 lds_trans_frag(const lds_char* stage, int lane_base, int db,
-                                                 int s2) {
-  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) v4i16*)(stage + lane_base + tr_const<D>(db, s2, 0)));
-  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) v4i16*)(stage + lane_base + tr_const<D>(db, s2, 1)));
-  typedef short v8i16 __attribute__((ext_vector_type(8)));
-  const v8i16 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-  return __builtin_bit_cast(bf16x8, both);
-}
-
-// One 32-row half block (S*1 KB) of a ROW-gathered tensor -> LDS, no VGPRs in between.
-template <int D>
-__device__ __forceinline__ void stage_half(__amdgpu_buffer_rsrc_t r, int soff, lds_char* dst,
-                                           int lane) {
-#pragma unroll
-  for (int s = 0; s < D / 16; ++s)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(dst + s * 1024),
-                                             16, lane * 16, soff + s * 1024, 0, 0);
-}
-
-// ---------------------------------------------------------------------------------------------
-// dQ (query-stationary): grid = B*Hh*cpx*8, one wave per query cube.  Per 32-key half cube:
-// K and V rows are staged straight into LDS (double buffered, the next tile in flight while this
-// one computes), S^T = K Q^T and dP^T = V dO^T take the K/V rows as A operands and Q, dO rows
-// (held in registers) as B operands; dS^T stays in the accumulator registers and, as bf16, is
-// the B operand of dQ^T += K^T dS^T, whose A operand is read transposed from the staged K rows.
-// ---------------------------------------------------------------------------------------------
-template <int D, bool RAGGED>
-__global__ __launch_bounds__(64) void bwd_dq_mfma_kernel(
-    Geom g, const bf16_t* __restrict__ q_row, const bf16_t* __restrict__ do_row,
-    const bf16_t* __restrict__ k_row, const bf16_t* __restrict__ v_row,
-    const float2* __restrict__ ld_c, const int32_t* __restrict__ idx, int k_sel, float scale,
-    float c_log2, int cpx, float* __restrict__ dq) {
-  constexpr int S = D / 16;
-  constexpr int DB = D / 32;
-  constexpr int cube_bytes = 64 * D * 2;
-  constexpr int half_bytes = 32 * D * 2;
-  __shared__ __attribute__((aligned(16))) char stage0[2 * half_bytes];  // K rows | V rows
-  __shared__ __attribute__((aligned(16))) char stage1[2 * half_bytes];
-
-  const int L = blockIdx.x;
-  const int xcd = L & 7;
-  const int k8 = L >> 3;
-  const int bh = k8 / cpx;
-  const int i = xcd * cpx + (k8 % cpx);
-  if (i >= g.nbq) return;
-  const int b = bh / g.Hh, h = bh % g.Hh;
-  const int lane = threadIdx.x;
-  const int l32 = lane & 31;
-  const int hh = lane >> 5;
-
-  const size_t bh_bytes = (size_t)g.nbk * cube_bytes;
-  const size_t bh_elems = (size_t)g.nbk * 64 * D;
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(k_row + bh * bh_elems, bh_bytes);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(v_row + bh * bh_elems, bh_bytes);
-  const int32_t* irow = idx + ((size_t)bh * g.nbq + i) * k_sel;
-  const int ntiles = 2 * k_sel;
-  lds_char* st0 = (lds_char*)stage0;
-  lds_char* st1 = (lds_char*)stage1;
-  {
-    const int off0 = irow[0] * cube_bytes;
-    stage_half<D>(rk, off0, st0, lane);
-    stage_half<D>(rv, off0, st0 + half_bytes, lane);
-  }
-
-  // Q and dO rows of this query cube as B operands (lane = query, 8 consecutive d).
-  const size_t q_bh = (size_t)bh * g.nbq * (64 * D);
-  const __amdgpu_buffer_rsrc_t rq = make_rsrc(q_row + q_bh, (size_t)g.nbq * cube_bytes);
-  const __amdgpu_buffer_rsrc_t rd = make_rsrc(do_row + q_bh, (size_t)g.nbq * cube_bytes);
-  bf16x8 qreg[2][S], dreg[2][S];
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-    for (int s = 0; s < S; ++s) {
-      qreg[qb][s] = bld16(rq, lane * 16, i * cube_bytes + (qb * S + s) * 1024);
-      dreg[qb][s] = bld16(rd, lane * 16, i * cube_bytes + (qb * S + s) * 1024);
-    }
-  float lse2[2], dl[2];
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const float2 ld = ld_c[((size_t)bh * g.nbq + i) * 64 + 32 * qb + l32];
-    lse2[qb] = ld.x;  // LSE in base 2
-    dl[qb] = ld.y;
-  }
-
-  f32x16 acc[DB][2];
-#pragma unroll
-  for (int db = 0; db < DB; ++db) { zero16(acc[db][0]); zero16(acc[db][1]); }
-  const int trb = tr_lane_base(lane);
-
-  auto tile = [&](int t, lds_char* cur, lds_char* nxt) {
-    // next tile's K and V rows -> the other stage (its previous reads were consumed last tile);
-    // the last tile re-stages itself so every tile waits the same way
-    const int tn = t + 1 < ntiles ? t + 1 : t;
-    const int noff = irow[tn >> 1] * cube_bytes + (tn & 1) * half_bytes;
-    stage_half<D>(rk, noff, nxt, lane);
-    stage_half<D>(rv, noff, nxt + half_bytes, lane);
-    __builtin_amdgcn_s_waitcnt(0x0f70 | ((2 * S) & 0xf) | (((2 * S) >> 4) << 14));  // vmcnt(2S)
-    f32x16 st[2], dpt[2];
-    zero16(st[0]); zero16(st[1]); zero16(dpt[0]); zero16(dpt[1]);
-    bf16x8 ka[S];
-#pragma unroll
-    for (int s = 0; s < S; ++s) ka[s] = lds_row_frag(cur, lane, s);
-#pragma unroll
-    for (int s = 0; s < S; ++s) {
-      st[0] = mfma32(ka[s], qreg[0][s], st[0]);
-      st[1] = mfma32(ka[s], qreg[1][s], st[1]);
-    }
-#pragma unroll
-    for (int s = 0; s < S; ++s) ka[s] = lds_row_frag(cur + half_bytes, lane, s);
-#pragma unroll
-    for (int s = 0; s < S; ++s) {
-      dpt[0] = mfma32(ka[s], dreg[0][s], dpt[0]);
-      dpt[1] = mfma32(ka[s], dreg[1][s], dpt[1]);
-    }
-    // Ragged grids need no key mask here: a key slot without a token has a zero K row in the
-    // gather, so its dS adds nothing to dQ = dS K as long as it is finite.  Its P = exp(-LSE)
-    // could overflow for a very negative LSE, so the ragged instantiation clamps P at 1 (a valid
-    // P is <= 1; the clamp only trims rounding).  A query slot without a token has LSE = +inf,
-    // so its P row is 0.
-    bf16x8 kt[DB * 2];
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) kt[db * 2 + s2] = lds_trans_frag<D>(cur, trb, db, s2);
-    bf16x8 dsb[2][2];
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int r = 8 * s2 + e;
-          float p = fast_exp2(fmaf(st[qb][r], c_log2, -lse2[qb]));
-          if constexpr (RAGGED) p = fminf(p, 1.0f);
-          dsb[s2][qb][e] = (__bf16)(p * (dpt[qb][r] - dl[qb]));
-        }
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        acc[db][0] = mfma32(kt[db * 2 + s2], dsb[s2][0], acc[db][0]);
-        acc[db][1] = mfma32(kt[db * 2 + s2], dsb[s2][1], acc[db][1]);
-      }
-  };
-  for (int t = 0; t < ntiles; t += 2) {
-    tile(t, st0, st1);
-    if (t + 1 < ntiles) tile(t + 1, st1, st0);
-  }
-  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the last re-staging has landed
-
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const int tq = cube_token(g, i, 32 * qb + l32);
-    if (tq < 0) continue;  // slot outside a ragged grid
-    float* out = dq + bnhd_offset(g, g.Nq, b, tq, h);
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int d = 32 * db + 8 * r4 + 4 * hh;
-        *reinterpret_cast<float4*>(out + d) =
-            make_float4(acc[db][qb][4 * r4] * scale, acc[db][qb][4 * r4 + 1] * scale,
-                        acc[db][qb][4 * r4 + 2] * scale, acc[db][qb][4 * r4 + 3] * scale);
-      }
-  }
-}
 
 // ---------------------------------------------------------------------------------------------
 // dK, dV (key-stationary over the CSR transpose): grid = B*Hh*(ccx+ncx)*8, one wave per key cube
@@ -413,24 +185,6 @@ __global__ __launch_bounds__(64) void bwd_dkdv_mfma_kernel(
   }
 }
 
-hipError_t launch_bwd_dq_mfma(const Geom& g, const bf16_t* q_row, const bf16_t* do_row,
-                              const bf16_t* k_row, const bf16_t* v_row, const float2* ld_c,
-                              const int32_t* idx, int k_sel, float scale, float* dq,
-                              hipStream_t s) {
-  const int cpx = (g.nbq + 7) / 8;
-  dim3 grid((unsigned)(g.B * g.Hh * cpx * 8));
-  const float c_log2 = scale * kLog2e;
-#define BSA_DQ(DD, RG)                                                                          \
-  hipLaunchKernelGGL((bwd_dq_mfma_kernel<DD, RG>), grid, dim3(64), 0, s, g, q_row, do_row, k_row, \
-                     v_row, ld_c, idx, k_sel, scale, c_log2, cpx, dq)
-  if (g.D == 64) {
-    if (g.ragged) BSA_DQ(64, true); else BSA_DQ(64, false);
-  } else {
-    if (g.ragged) BSA_DQ(128, true); else BSA_DQ(128, false);
-  }
-#undef BSA_DQ
-  return hipGetLastError();
-}
 
 hipError_t launch_bwd_dkdv_mfma(const Geom& g, const bf16_t* k_row, const bf16_t* v_row,
                                 const bf16_t* q_row, const bf16_t* do_row, const float2* ld_c,
