@@ -118,6 +118,8 @@ def main() -> int:
                     help="skip the fused QK-norm + 3D RoPE prologue measurement")
     ap.add_argument("--no-dense", action="store_true",
                     help="skip the dense-attention (r = all) forward comparison")
+    ap.add_argument("--no-480p", action="store_true",
+                    help="skip the 480p-class forward + backward step")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -246,6 +248,8 @@ def main() -> int:
         "roofline": roofline,
     }
 
+    if not args.no_480p:
+        out["step_480p"] = bench_480p(bsa, synth, torch, dev)
     if not args.no_continuation:
         out["continuation_fwd"] = bench_continuation(bsa, synth, orc, torch, dev, args)
     if not args.no_dense:
@@ -366,6 +370,72 @@ def _time_fwd(bsa, torch, p, t, r, reps=3):
     tot = [sum(ms for _, ms in ev.elapsed_all()) for ev in evs]
     del ws, idx
     return ks, float(np.median(tot))
+
+
+def bench_480p(bsa, synth, torch, dev, reps=5):
+    """The headline step (pool x2, select, forward, backward) at the 480p-class grid 24x32x52
+    (QKNorm q/k, top-r = 62, dO ~ N(0,1)): per-call ms from HIP events on the launch stream."""
+    import numpy as np
+    w = synth.workload(5)
+    log(f"drawing inputs for {w.name}")
+    x = synth.make_inputs(w)
+    t = {k: torch.from_numpy(v).to(dev).to(torch.bfloat16) for k, v in x.items()}
+    del x
+    p = bsa.Problem(**w.shape_dict)
+    ks = bsa.bsa_num_selected(p, w.r)
+    scale = 1.0 / math.sqrt(p.head_dim)
+    ws_f = torch.empty(bsa.bsa_workspace_bytes(p, torch.bfloat16, ks, False), dtype=torch.uint8,
+                       device=dev)
+    ws_b = torch.empty(bsa.bsa_workspace_bytes(p, torch.bfloat16, ks, True), dtype=torch.uint8,
+                       device=dev)
+    qm = torch.empty((p.batch, p.heads, p.nbq, p.head_dim), dtype=torch.float32, device=dev)
+    km = torch.empty_like(qm)
+    idx = torch.empty((p.batch, p.heads, p.nbq, ks), dtype=torch.int32, device=dev)
+    o = torch.empty_like(t["q"])
+    lse = torch.empty((p.batch, p.heads, p.Nq), dtype=torch.float32, device=dev)
+    dq = torch.empty(t["q"].shape, dtype=torch.float32, device=dev)
+    dk, dv = torch.empty_like(dq), torch.empty_like(dq)
+
+    def step(ev):
+        calls = [lambda: bsa.bsa_block_pool(p, t["q"], qm),
+                 lambda: bsa.bsa_block_pool(p, t["k"], km),
+                 lambda: bsa.bsa_select_topr(p, qm, km, w.r, with_mask=False, idx=idx),
+                 lambda: bsa.bsa_sparse_attn_fwd(p, t["q"], t["k"], t["v"], idx, ks, scale, o=o,
+                                                 lse=lse, workspace=ws_f),
+                 lambda: bsa.bsa_sparse_attn_bwd(p, t["q"], t["k"], t["v"], o, t["dO"], lse, idx,
+                                                 ks, scale, dq=dq, dk=dk, dv=dv, workspace=ws_b)]
+        for e, c in zip(ev, calls):
+            with e:
+                c()
+
+    step([bsa.StageEvents(8) for _ in range(5)])
+    torch.cuda.synchronize()
+    evs = [[bsa.StageEvents(8) for _ in range(5)] for _ in range(reps)]
+    for ev in evs:
+        step(ev)
+    torch.cuda.synchronize()
+    stage: dict[str, list] = {}
+    for ev in evs:
+        per = {}
+        for e in ev:
+            for name, ms in e.elapsed_all():
+                per[name] = per.get(name, 0.0) + ms
+        for name, ms in per.items():
+            stage.setdefault(name, []).append(ms)
+    med = {k: float(np.median(v)) for k, v in stage.items()}
+    fwd_ms = med.get("gather_qkv", 0.0) + med.get("attn_fwd_mfma", 0.0)
+    bwd_ms = sum(med.get(k, 0.0) for k in ("bwd_prep", "gather_qkv_do", "bwd_dkdv_mfma",
+                                            "bwd_dq_mfma"))
+    step_ms = sum(med.values())
+    f = fwd_flops(p, ks)
+    return {"workload": "480p-class BSA fwd+bwd: B=1, Hh=32, D=128, grid 24x32x52, cube 4x4x4, "
+                        "top-r=62 + own cube, QKNorm q/k, dO~N(0,1)",
+            "k_sel": ks, "fwd_tflop": round(f / 1e12, 3),
+            "step_ms": round(step_ms, 3), "fwd_ms": round(fwd_ms, 3), "bwd_ms": round(bwd_ms, 3),
+            "value_tflops": round(3.5 * f / (step_ms * 1e-3) / 1e12, 1),
+            "fwd_tflops": round(f / (fwd_ms * 1e-3) / 1e12, 1),
+            "bwd_tflops_effective": round(2.5 * f / (bwd_ms * 1e-3) / 1e12, 1),
+            "stages_ms_per_step": {k: round(v, 4) for k, v in med.items()}}
 
 
 def bench_ragged(bsa, synth, torch, dev, args, reps=3):
