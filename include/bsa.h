@@ -24,7 +24,8 @@
  *    gradients) hold only the NOISE segment, i.e. the last T - cond_T frames, so N = Nq =
  *    (T - cond_T)*H*W.  k_cache / v_cache hold the first cond_T frames: N = Nc = cond_T*H*W.
  *  Cubes.  A cube is ct x ch x cw tokens (c = ct*ch*cw).  Cube coordinates (a, b, e) =
- *    (t/ct, h/ch, w/cw) inside a segment; the cube id inside a segment is (a*(H/ch) + b)*(W/cw) + e.
+ *    (t/ct, h/ch, w/cw) inside a segment; the cube id inside a segment is a*gh*gw + b*gw + e
+ *    with gh = ceil(H/ch), gw = ceil(W/cw) cubes along h and w.
  *    Key cube ids put the nbc condition cubes first (0..nbc-1) and the nbq noise cubes after them
  *    (nbc..nbc+nbq-1); query cube i is key cube nbc+i.  nbk = nbc + nbq.
  *  Pooled tensors are [B, Hh, nbq, D] fp32.  idx is [B, Hh, nbq, k_sel] int32, each row ascending.
@@ -67,10 +68,11 @@ typedef enum { BSA_F32 = 0, BSA_BF16 = 1 } bsa_dtype_t;
  * Requirements: all sizes > 0 except cond_T >= 0; head_dim in {64, 128}; T - cond_T and cond_T
  * divisible by cube_t, cond_T < T; cube size c = cube_t*cube_h*cube_w <= 256; at most 39808
  * cubes per segment (the selection keeps one row of keys in LDS), and for the backward at most
- * 39936 key cubes (condition + noise) in all.  H and W need not be multiples of cube_h, cube_w (ragged latent grids such
- * as the 45-token height of 720p): the last cube row / column then keeps only the tokens of its
- * box that lie inside the grid -- its mean divides by that count and its missing slots are
- * neither keys nor queries.  Cube counts are ceil(H/cube_h) * ceil(W/cube_w) per cube layer. */
+ * 39936 key cubes (condition + noise) in all.  H and W need not be multiples of cube_h, cube_w
+ * (ragged latent grids such as the 45-token height of 720p): the last cube row / column then
+ * keeps only the tokens of its box that lie inside the grid -- its mean divides by that count
+ * and its missing slots are neither keys nor queries.  Cube counts are ceil(H/cube_h) *
+ * ceil(W/cube_w) per cube layer. */
 typedef struct {
   int32_t batch, heads, head_dim; /* B, Hh, D                                  */
   int32_t T, H, W;                /* latent grid, condition frames included    */
