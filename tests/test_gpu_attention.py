@@ -257,6 +257,41 @@ def test_bwd_full_size_sampled():
     assert np.abs(dk.astype(np.float64).sum(axis=1)).max() < 0.5
 
 
+def test_bwd_720p_full_size_sampled():
+    """The backward of the headline step exactly as the benchmark runs it: 720p-class grid
+    24x48x80, 32 heads, top-144, the same seeded inputs (q, k, v, dO) and the library's default
+    launch configuration; sampled query cubes (dQ) and key cubes (dK, dV) against the oracle, and
+    the full-size sum properties."""
+    w, x = cached_inputs(3, (("with_grad", True),))
+    print_case(f"bwd full {w.name} (benchmark inputs)")
+    p = bsa.Problem(**w.shape_dict)
+    op = orc.Problem(**w.shape_dict)
+    t = {k: to_dev(v, w.dtype) for k, v in x.items()}
+    idx_d = _gpu_selection(w, t, p)
+    ks = orc.num_selected(op, w.r)
+    scale = scale_of(op)
+    o, lse = bsa.bsa_sparse_attn_fwd(p, t["q"], t["k"], t["v"], idx_d, ks, scale)
+    dq, dk, dv = bsa.bsa_sparse_attn_bwd(p, t["q"], t["k"], t["v"], o, t["dO"], lse, idx_d, ks,
+                                         scale)
+    del t, o, lse
+    idx = idx_d.cpu().numpy()
+    dq, dk, dv = (a.cpu().numpy() for a in (dq, dk, dv))
+    rows = sample_rows(op, [0, 17, 31], 3, seed=21)
+    cols = sample_rows(op, [0, 17, 31], 3, seed=22)
+    rq, rk, rv = orc.attn_bwd(x["q"], x["k"], x["v"], x["dO"], idx, op, scale, rows=rows,
+                              key_cubes=cols)
+    toks = orc.noise_cube_tokens(op)
+    assert_close(np.stack([dq[b, toks[i], h] for (b, h, i) in rows]),
+                 np.stack([rq[k] for k in rows]), "bf16", "dQ")
+    assert_close(np.stack([dk[b, toks[j], h] for (b, h, j) in cols]),
+                 np.stack([rk[k] for k in cols]), "bf16", "dK")
+    assert_close(np.stack([dv[b, toks[j], h] for (b, h, j) in cols]),
+                 np.stack([rv[k] for k in cols]), "bf16", "dV")
+    dO64 = x["dO"].astype(np.float64)
+    np.testing.assert_allclose(dv.sum(axis=1), dO64.sum(axis=1), atol=0.5, rtol=1e-2)
+    assert np.abs(dk.astype(np.float64).sum(axis=1)).max() < 0.5
+
+
 # ---------------------------------------------------------------------------------------------
 # Backward with the condition cache (continuation training): cache gradients included.
 # ---------------------------------------------------------------------------------------------
