@@ -17,8 +17,9 @@
 //  * Lazy rescale: the running max only moves when a tile's max exceeds it by more than 8 (base 2),
 //    so P <= 256 and the O accumulators are rescaled rarely; the result is exact either way
 //    because O and l are always scaled by the same exp2(m_used).
-//  * Next tile's K is requested right after this tile's S MFMAs, next V right after the PV
-//    MFMAs; about 230 live VGPRs, so two waves share each SIMD and hide each other's latency.
+//  * Next tile's V (and K) is requested right after this tile's PV MFMAs -- at D = 64 the next K
+//    already after the S MFMAs, a longer lead that D = 128 has no registers for; about 245 live
+//    VGPRs at D = 128, so two waves share each SIMD and hide each other's latency.
 //  * Work order is head-major (all XCDs work on the same (b, h) at a time, keeping that head's
 //    K/V hot in the shared Infinity Cache) and XCD-aware: workgroup L runs on XCD L%8, which gets
 //    a contiguous run of query cubes of the head (spatial neighbours select similar key cubes).
