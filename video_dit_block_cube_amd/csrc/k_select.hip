@@ -7,9 +7,10 @@
 // same-table analogy).  Score S[i,j] = D^-1/2 <q_mean_i, k_mean_j> in fp32; order is score
 // descending, then cube id ascending; -0.0 counts as +0.0.
 //
-// MI355X design: a 256-lane workgroup owns R query rows of one (b, h).  Phase 1 writes the R x nbq
-// scores into LDS as order-preserving uint32 keys (every column's dot product runs in the same
-// d order, so equal descriptors give bitwise-equal scores and exact ties stay exact).  Phase 2:
+// MI355X design: a 256-lane workgroup owns R query rows of one (b, h).  Phase 1 computes the R x nbq
+// scores on fp32 MFMA (v_mfma_f32_16x16x4f32, 16 key cubes per wave step) and writes them into LDS
+// as order-preserving uint32 keys (every score is summed over d in the same order, so equal
+// descriptors give bitwise-equal scores and exact ties stay exact).  Phase 2:
 // one wave per row runs a 4-pass MSB-first radix select (8-bit digits, LDS histogram, wave suffix
 // scan with shuffles) to find the r-th largest key T and how many keys equal to T to take; the
 // lower-id rule among equal keys falls out of walking the ids in ascending order.  Phase 3 walks
@@ -47,33 +48,53 @@ __global__ __launch_bounds__(256) void select_kernel(Geom g, const float* __rest
   const float* qbase = qm + (size_t)bh * nbq * D;
   const float* kbase = km + (size_t)bh * nbq * D;
 
-  // Phase 1: scores -> order keys in LDS.
+  // Phase 1: scores -> order keys in LDS, on v_mfma_f32_16x16x4f32.  A = the R query
+  // descriptors (rows R..15 zero), B = 16 key descriptors per step of a wave.  The contraction
+  // index is permuted the same way on both sides: at step (c, e) lane group grp = lane/16 holds
+  // d = 16c + 4grp + e, so each lane's operands are float4 reads (a key row's four lane groups read
+  // 64 contiguous bytes) and every score is summed over d in one fixed order.
   for (int e = tid; e < R * D; e += 256) {
     const int r = e / D;
     qs[e] = (row0 + r < nbq) ? qbase[(size_t)(row0 + r) * D + (e % D)] : 0.f;
   }
   __syncthreads();
   const float scale = 1.0f / sqrtf((float)D);
-  for (int j = tid; j < nbq; j += 256) {
-    float acc[R];
+  {
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    const int m = lane & 15, grp = lane >> 4;
+    const int nc = D / 16;  // 4 or 8
+    const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+    f32x4 qa[8];
 #pragma unroll
-    for (int r = 0; r < R; ++r) acc[r] = 0.f;
-    const float4* kr = reinterpret_cast<const float4*>(kbase + (size_t)j * D);
-    for (int d4 = 0; d4 < D / 4; ++d4) {
-      const float4 kv = kr[d4];
+    for (int c = 0; c < 8; ++c)
+      qa[c] = (c < nc && m < R)
+                  ? *reinterpret_cast<const f32x4*>(qs + m * D + 16 * c + 4 * grp)
+                  : zero4;
+    for (int jb = wave * 16; jb < nbq; jb += 64) {
+      const int n = jb + m;  // this lane's key cube (B column)
+      f32x4 kb[8];
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const float4 qv = reinterpret_cast<const float4*>(qs + r * D)[d4];
-        acc[r] = fmaf(qv.x, kv.x, acc[r]);
-        acc[r] = fmaf(qv.y, kv.y, acc[r]);
-        acc[r] = fmaf(qv.z, kv.z, acc[r]);
-        acc[r] = fmaf(qv.w, kv.w, acc[r]);
+      for (int c = 0; c < 8; ++c)
+        kb[c] = (c < nc && n < nbq)
+                    ? *reinterpret_cast<const f32x4*>(kbase + (size_t)n * D + 16 * c + 4 * grp)
+                    : zero4;
+      f32x4 acc = zero4;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        if (c < nc) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[c][e], kb[c][e], acc, 0, 0, 0);
+        }
       }
-    }
+      // lane holds rows 4*grp + i of the 16 x 16 block, column m
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const int i = row0 + r;
-      keys[(size_t)r * nbq + j] = (i == j) ? 0u : order_key(acc[r] * scale);
+      for (int i = 0; i < 4; ++i) {
+        const int r = 4 * grp + i;
+        if (r < R && n < nbq)
+          keys[(size_t)r * nbq + n] = (row0 + r == n) ? 0u : order_key(acc[i] * scale);
+      }
     }
   }
   __syncthreads();
