@@ -365,3 +365,13 @@ def test_bwd_condition_cache_full_size_sampled():
         < 0.5
     # every cache row receives gradient (all noise queries attend every condition cube)
     assert np.all(np.abs(dvc).sum(axis=-1) > 0)
+    # sampled condition cubes of one head against the oracle: each one's dK/dV sums over all 720
+    # query cubes (the longest items of the key-stationary pass)
+    cols = [(0, 9, 0), (0, 9, 361), (0, 9, op.nbc - 1)]
+    rk, rv = orc.attn_bwd(x["q"], x["k"], x["v"], dO, idx, op, scale, key_cubes=cols,
+                          k_cache=x["k_cache"], v_cache=x["v_cache"])[1:3]
+    ctoks = orc.cond_cube_tokens(op)
+    assert_close(np.stack([dkc[b, ctoks[j], h] for (b, h, j) in cols]),
+                 np.stack([rk[c] for c in cols]), "bf16", "dK_cache")
+    assert_close(np.stack([dvc[b, ctoks[j], h] for (b, h, j) in cols]),
+                 np.stack([rv[c] for c in cols]), "bf16", "dV_cache")
