@@ -1,0 +1,53 @@
+"""Run-to-run determinism: every stage of the path (pool, select, forward with its key-range
+split, backward including condition-cache gradients) is free of atomics and of timing-dependent
+summation orders, so two calls on the same inputs must agree bit for bit."""
+import numpy as np
+import pytest
+
+import oracle as orc
+from tests._util import print_case, scale_of, to_dev
+from video_dit_block_cube_amd import bsa, synth
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(p, t, r, ks, scale):
+    qm = bsa.bsa_block_pool(p, t["q"])
+    km = bsa.bsa_block_pool(p, t["k"])
+    idx, mask = bsa.bsa_select_topr(p, qm, km, r)
+    o, lse = bsa.bsa_sparse_attn_fwd(p, t["q"], t["k"], t["v"], idx, ks, scale,
+                                     t.get("k_cache"), t.get("v_cache"))
+    grads = bsa.bsa_sparse_attn_bwd(p, t["q"], t["k"], t["v"], o, t["dO"], lse, idx, ks, scale,
+                                    k_cache=t.get("k_cache"), v_cache=t.get("v_cache"))
+    if not isinstance(grads, tuple):
+        grads = (grads,)
+    import torch
+    outs = [qm, km, idx, mask, o, lse, *grads]
+    # bf16 has no numpy type: compare its raw 16-bit patterns
+    return [(a.view(torch.int16) if a.dtype == torch.bfloat16 else a).cpu().numpy() for a in outs]
+
+
+@pytest.mark.parametrize("number, over, splits", [
+    (5, (("heads", 4),), None),                                  # 480p grid, default 8-range split
+    (4, (("heads", 2), ("T", 12), ("H", 24), ("W", 40), ("cond_T", 4)), None),  # continuation
+    (5, (("heads", 2), ("H", 30), ("W", 50)), "16"),             # ragged grid, 16 ranges
+])
+def test_bit_identical_reruns(number, over, splits, monkeypatch):
+    if splits is not None:
+        monkeypatch.setenv("BSA_FWD_SPLITS", splits)
+    w = synth.workload(number, **dict(over))
+    print_case(f"determinism {w.name} {dict(over)} splits={splits}")
+    x = synth.make_inputs(w)
+    if "dO" not in x:
+        x["dO"] = synth.round_to_bf16(
+            np.random.default_rng(77).standard_normal(x["q"].shape).astype(np.float32))
+    p, op = bsa.Problem(**w.shape_dict), orc.Problem(**w.shape_dict)
+    t = {k: to_dev(v, w.dtype) for k, v in x.items()}
+    ks, scale = orc.num_selected(op, w.r), scale_of(op)
+    first = _run(p, t, w.r, ks, scale)
+    second = _run(p, t, w.r, ks, scale)
+    names = ["q_mean", "k_mean", "idx", "mask", "O", "LSE", "dQ", "dK", "dV", "dK_cache",
+             "dV_cache"]
+    for name, a, b in zip(names, first, second):
+        assert a.dtype == b.dtype and a.shape == b.shape, name
+        assert a.tobytes() == b.tobytes(), f"{name} differs between two identical calls"
