@@ -47,6 +47,21 @@ def kernel_flops(name: str, p, k_sel: int) -> float | None:
             "bwd_dq_mfma": 3 * one_gemm}.get(name)   # S, dP, dQ
 
 
+def stage_bytes(name: str, p, k_sel: int) -> float | None:
+    """Algorithmic HBM bytes of one call of a bandwidth-bound stage at a divisible grid with no
+    condition frames (each tensor read or written once): bf16 token tensors, fp32 means and
+    Delta/LSE, gathered cube-major copies of the same size as their source."""
+    tensor = p.batch * p.Nq * p.heads * p.head_dim * 2          # one bf16 [B, Nq, Hh, D]
+    means = p.batch * p.heads * p.nbq * p.head_dim * 4
+    per_query = p.batch * p.heads * p.Nq * 4                    # one fp32 value per query token
+    idx = p.batch * p.heads * p.nbq * k_sel * 4                  # int32 selection
+    return {"pool": tensor + means,                             # x in, means out
+            "gather_qkv": 3 * 2 * tensor,                       # q, k, v in; ROW/TRANS copies out
+            "gather_qkv_do": 4 * 2 * tensor,                    # q, k, v, dO in; ROW copies out
+            # O, dO in; LSE, Delta (+ pairs) out; CSR transpose: idx in, lists out
+            "bwd_prep": 2 * tensor + 4 * per_query + 2 * idx}.get(name)
+
+
 def traffic_from_profile(stage: str):
     """HBM bytes per launch measured by rocprofv3 counters (profiles/traffic_<stage>.txt), or None
     when no measurement exists or the kernel source changed since it was taken."""
@@ -220,12 +235,17 @@ def main() -> int:
     per_kernel = {}
     for k, v in avg.items():
         kf = kernel_flops(k, p, ks)
+        kb = stage_bytes(k, p, ks)
         per_kernel[k] = {"avg_ms": round(v, 4),
                          "median_ms": round(float(np.median(stage_ms[k])), 4),
                          "p90_ms": round(float(np.percentile(stage_ms[k], 90)), 4),
                          **({"tflops": round(kf / (v * 1e-3) / 1e12, 1),
                              "frac_peak": round(kf / (v * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
-                            if kf else {})}
+                            if kf else {}),
+                         **({"algorithmic_GB": round(kb / 1e9, 3),
+                             "achieved_GBps": round(kb / (v * 1e-3) / 1e9, 1),
+                             "frac_hbm_peak": round(kb / (v * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+                            if kb else {})}
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 3),
