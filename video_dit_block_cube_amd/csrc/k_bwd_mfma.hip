@@ -21,9 +21,10 @@ namespace bsa {
 // (condition cubes, read from the cache and written to the cache gradients, and noise cubes).
 // K and V rows of the key cube are B operands held
 // in registers; per 32-query half of each query cube that selected j, the Q and dO rows are staged
-// straight into LDS (double buffered), S = Q K^T and dP = dO V^T read them as A operands, and
-// P, dS built in place in the accumulators are the B operands of dV^T += dO^T P and
-// dK^T += Q^T dS, whose A operands are read transposed from the same staged rows.
+// straight into LDS (double buffered), S = Q K^T and dP = dO V^T read them as A operands (each
+// row fragment read once and applied to both 32-key halves), and P, dS built in place in the
+// accumulators are the B operands of dV^T += dO^T P and dK^T += Q^T dS, whose A operands are
+// read transposed from the same staged rows.
 // ---------------------------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(64) void bwd_dkdv_mfma_kernel(
@@ -106,35 +107,59 @@ __global__ __launch_bounds__(64) void bwd_dkdv_mfma_kernel(
     const int tn = t + 1 < nsteps ? t + 1 : t;
     stage_step(csr_list[beg + (tn >> 1)], tn & 1, nxt);
     __builtin_amdgcn_s_waitcnt(0x0f70 | ((2 * S + 1) & 0xf) | (((2 * S + 1) >> 4) << 14));
-    // P and dS, key half by key half (rows 8*r4 + 4*hh + e4 of the 32-query half per lane)
-    bf16x8 pb[2][2], dsb[2][2];
     const __attribute__((address_space(3))) f32x4* ldp =
         (const __attribute__((address_space(3))) f32x4*)(cur + 2 * half_bytes);
+    // S = Q K^T for both key halves: each staged Q row fragment is read once
+    f32x16 sc[2];
+    zero16(sc[0]);
+    zero16(sc[1]);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      // re-read the staged rows for each key half instead of keeping 32 fragments live
-      asm volatile("" ::: "memory");
-      f32x16 st, dp;
-      zero16(st);
-      zero16(dp);
+    for (int s = 0; s < S; ++s) {
+      const bf16x8 a = lds_row_frag(cur, lane, s);
+      sc[0] = mfma32(a, kreg[0][s], sc[0]);
+      sc[1] = mfma32(a, kreg[1][s], sc[1]);
+    }
+    // P = exp2(S*scale*log2(e) - LSE2) in place (rows 8*r4 + 4*hh + e4 of the half per lane),
+    // with its bf16 copy as the B operand of dV^T; the exponentials overlap dP's MFMAs
+    bf16x8 pb[2][2], dsb[2][2];
 #pragma unroll
-      for (int s = 0; s < S; ++s) st = mfma32(lds_row_frag(cur, lane, s), kreg[kb][s], st);
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const f32x4 p01 = ldp[(8 * r4 + 4 * hh) / 2];
+      const f32x4 p23 = ldp[(8 * r4 + 4 * hh) / 2 + 1];
+      const float lv[4] = {p01[0], p01[2], p23[0], p23[2]};
 #pragma unroll
-      for (int s = 0; s < S; ++s)
-        dp = mfma32(lds_row_frag(cur + half_bytes, lane, s), vreg[kb][s], dp);
+      for (int e4 = 0; e4 < 4; ++e4) {
+        const int r = 4 * r4 + e4;
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        // pairs (base-2 lse, delta) of rows 8*r4 + 4*hh + 0..3
-        const f32x4 p01 = ldp[(8 * r4 + 4 * hh) / 2];
-        const f32x4 p23 = ldp[(8 * r4 + 4 * hh) / 2 + 1];
-        const float lv[4] = {p01[0], p01[2], p23[0], p23[2]};
-        const float dv4[4] = {p01[1], p01[3], p23[1], p23[3]};
-#pragma unroll
-        for (int e4 = 0; e4 < 4; ++e4) {
-          const int r = 4 * r4 + e4;
-          const float p = fast_exp2(fmaf(st[r], c_log2, -lv[e4]));
+        for (int kb = 0; kb < 2; ++kb) {
+          const float p = fast_exp2(fmaf(sc[kb][r], c_log2, -lv[e4]));
+          sc[kb][r] = p;  // P in fp32 for dS
           pb[kb][r >> 3][r & 7] = (__bf16)p;
-          dsb[kb][r >> 3][r & 7] = (__bf16)(p * (dp[r] - dv4[e4]));
+        }
+      }
+    }
+    // dP = dO V^T for both key halves, then dS = P o (dP - Delta)
+    f32x16 dp[2];
+    zero16(dp[0]);
+    zero16(dp[1]);
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      const bf16x8 a = lds_row_frag(cur + half_bytes, lane, s);
+      dp[0] = mfma32(a, vreg[0][s], dp[0]);
+      dp[1] = mfma32(a, vreg[1][s], dp[1]);
+    }
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const f32x4 p01 = ldp[(8 * r4 + 4 * hh) / 2];
+      const f32x4 p23 = ldp[(8 * r4 + 4 * hh) / 2 + 1];
+      const float dv4[4] = {p01[1], p01[3], p23[1], p23[3]};
+#pragma unroll
+      for (int e4 = 0; e4 < 4; ++e4) {
+        const int r = 4 * r4 + e4;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const float p = sc[kb][r];
+          dsb[kb][r >> 3][r & 7] = (__bf16)(p * (dp[kb][r] - dv4[e4]));
         }
       }
     }
