@@ -476,26 +476,49 @@ def bench_ragged(bsa, synth, torch, dev, args, reps=3):
     wsb = torch.empty(bsa.bsa_workspace_bytes(p, torch.bfloat16, ks, True), dtype=torch.uint8,
                       device=dev)
 
-    def step():
-        qm = bsa.bsa_block_pool(p, t["q"])
-        km = bsa.bsa_block_pool(p, t["k"])
-        idx, _ = bsa.bsa_select_topr(p, qm, km, w.r, with_mask=False)
-        o, lse = bsa.bsa_sparse_attn_fwd(p, t["q"], t["k"], t["v"], idx, ks, scale, workspace=wsf)
-        bsa.bsa_sparse_attn_bwd(p, t["q"], t["k"], t["v"], o, t["dO"], lse, idx, ks, scale,
-                                workspace=wsb)
+    qm = torch.empty((p.batch, p.heads, p.nbq, p.head_dim), dtype=torch.float32, device=dev)
+    km = torch.empty_like(qm)
+    idx = torch.empty((p.batch, p.heads, p.nbq, ks), dtype=torch.int32, device=dev)
+    o = torch.empty_like(t["q"])
+    lse = torch.empty((p.batch, p.heads, p.Nq), dtype=torch.float32, device=dev)
+    dq, dk, dv = (torch.empty(shp, dtype=torch.float32, device=dev) for _ in range(3))
+
+    def step(ev=None):
+        calls = [
+            lambda: bsa.bsa_block_pool(p, t["q"], qm),
+            lambda: bsa.bsa_block_pool(p, t["k"], km),
+            lambda: bsa.bsa_select_topr(p, qm, km, w.r, with_mask=False, idx=idx),
+            lambda: bsa.bsa_sparse_attn_fwd(p, t["q"], t["k"], t["v"], idx, ks, scale, o=o,
+                                            lse=lse, workspace=wsf),
+            lambda: bsa.bsa_sparse_attn_bwd(p, t["q"], t["k"], t["v"], o, t["dO"], lse, idx, ks,
+                                            scale, dq=dq, dk=dk, dv=dv, workspace=wsb),
+        ]
+        for ci, c in enumerate(calls):
+            if ev is None:
+                c()
+            else:
+                with ev[ci]:
+                    c()
 
     step()
     torch.cuda.synchronize()
     ms = []
+    stage_ms: dict = {}
     for _ in range(reps):
+        ev = [bsa.StageEvents(8) for _ in range(5)]
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
-        step()
+        step(ev)
         e1.record()
         e1.synchronize()
         ms.append(e0.elapsed_time(e1))
+        for ci in range(5):
+            for name, v in ev[ci].elapsed_all():
+                stage_ms.setdefault(name, []).append(v)
     return {"grid": "24x45x80 (45 = 11 full cube rows + 1 row of height 1)", "k_sel": ks,
             "step_ms": round(float(np.median(ms)), 3),
+            # per step (pool runs twice)
+            "stages_ms_per_step": {k: round(float(np.sum(v)) / reps, 4) for k, v in stage_ms.items()},
             "note": "pool x2, select, fwd, bwd; partial edge cubes masked in the kernels"}
 
 

@@ -148,11 +148,11 @@ int fwd_splits(const Geom& g, int k_sel) {
 }
 
 // Forward workspace (MFMA path): K rows + V^T over all nbk key cubes, Q rows over the nbq query
-// cubes, then the key-range partials.
+// cubes, the key-range partials, then (ragged grids) the key cubes' slot masks.
 size_t fwd_ws(const Geom& g, bool mfma, int k_sel) {
   if (!mfma) return 0;
   return 2 * align_up(gather_bytes(g, true)) + align_up(gather_bytes(noise_only(g), true)) +
-         align_up(fwd_split_bytes(g, fwd_splits(g, k_sel)));
+         align_up(fwd_split_bytes(g, fwd_splits(g, k_sel))) + align_up(fwd_kmask_bytes(g));
 }
 
 template <typename F>
@@ -277,8 +277,11 @@ bsa_status_t bsa_sparse_attn_fwd(const bsa_problem_t* p, bsa_dtype_t dtype, cons
       if (st != BSA_OK) return st;
       stages.done("gather_qkv");
       const int ns = fwd_splits(g, k_sel);
+      uint2* kmask = g.ragged ? reinterpret_cast<uint2*>(static_cast<char*>(split_ws) +
+                                                         align_up(fwd_split_bytes(g, ns)))
+                              : nullptr;
       st = hip_status(launch_fwd_mfma(g, qrow, krow, vtr, idx, k_sel, softmax_scale, o, lse, ns,
-                                      split_ws, stream),
+                                      split_ws, kmask, stream),
                       "attention forward launch");
       stages.done("attn_fwd_mfma");
     } else {

@@ -58,12 +58,17 @@ hipError_t launch_gather(const Geom& g, const void* x, const void* x_cache, int 
 // k_attn_mfma.hip: bf16 MFMA forward for c == 64, D in {64, 128}; q_row is Q in the ROW gather
 // layout over the nbq query cubes ([B, Hh, nbq, 64*D]).  ns <= 1 runs one pass per
 // query cube; ns > 1 splits the key cube ids into ns ranges (one XCD's L2 per range) and merges
-// the partials, which need fwd_split_bytes(g, ns) bytes of split_ws.
+// the partials, which need fwd_split_bytes(g, ns) bytes of split_ws.  On a ragged grid kmask
+// points at fwd_kmask_bytes(g) bytes the launch fills with every key cube's slot mask (null and
+// unused otherwise).
 int fwd_split_ranges(const Geom& g, int k_sel, int requested);
 size_t fwd_split_bytes(const Geom& g, int ns);
 hipError_t launch_fwd_mfma(const Geom& g, const bf16_t* q_row, const bf16_t* k_row,
                            const bf16_t* v_trans, const int32_t* idx, int k_sel, float scale,
-                           void* o, float* lse, int ns, void* split_ws, hipStream_t s);
+                           void* o, float* lse, int ns, void* split_ws, uint2* kmask,
+                           hipStream_t s);
+// Bytes of the per-key-cube slot-mask table the MFMA forward needs on a ragged grid (else 0).
+size_t fwd_kmask_bytes(const Geom& g);
 
 // k_bwd_mfma.hip (dK/dV), k_bwd_dq.hip (dQ): bf16 MFMA backward kernels for c == 64, D in
 // {64, 128}; every operand comes from the ROW gather layout (transposed operands are read from

@@ -88,6 +88,13 @@ __device__ __forceinline__ bf16x8 pack8(const f32x16& a, int base) {
 
 }  // namespace
 
+// Slot mask of key cube j's 32-key half `half` from the per-launch table (ragged grids).
+__device__ __forceinline__ uint32_t key_half_mask(const uint2* __restrict__ kmask, int j,
+                                                  int half) {
+  const uint2 m = kmask[j];
+  return half ? m.y : m.x;
+}
+
 // Online-softmax attention of one 64-token query cube over the 32-key half cubes
 // [t_begin, t_end) of its (ascending) selection row, where row position p stands for entry
 // p + (p >= p_split ? p_skip : 0) (two disjoint spans walked as one; p_skip = 0 for one span).
@@ -99,17 +106,20 @@ __device__ __forceinline__ void attend_span(const Geom& g, const bf16x8* __restr
                                             __amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv,
                                             const int32_t* __restrict__ irow, int t_begin,
                                             int t_end, int p_split, int p_skip, float c_log2,
-                                            int lane, f32x16 (&acc)[D / 32][2],
-                                            float (&m_run)[2], float (&l_part)[2]) {
+                                            const uint2* __restrict__ kmask, int lane,
+                                            f32x16 (&acc)[D / 32][2], float (&m_run)[2],
+                                            float (&l_part)[2]) {
   constexpr int S = D / 16;
   constexpr int DB = D / 32;
   constexpr int cube_bytes = 64 * D * 2;
   const int vlane = lane * 16;
-  int cur_j;  // key cube id of tile t
+  int cur_j;                   // key cube id of tile t
+  uint32_t km_cur = ~0u;       // its slot mask (RAGGED): bit k set iff key slot k holds a token
   bf16x8 kr[S], vr[DB * 2];
   {
     const int p0 = t_begin >> 1;
     cur_j = irow[p0 + (p0 >= p_split ? p_skip : 0)];
+    if constexpr (RAGGED) km_cur = key_half_mask(kmask, cur_j, t_begin & 1);
     const int off0 = cur_j * cube_bytes + (t_begin & 1) * (32 * D * 2);
 #pragma unroll
     for (int s = 0; s < S; ++s) kr[s] = bld16(rk, vlane, off0 + s * 1024);
@@ -135,12 +145,12 @@ __device__ __forceinline__ void attend_span(const Geom& g, const bf16x8* __restr
     }
     if constexpr (RAGGED) {
       // accumulator row 8*(e/4) + 4*(lane/32) + e%4 of S^T is key slot 32*(t&1) + that row
-      const uint32_t km = cube_half_mask(g, cur_j < g.nbc ? cur_j : cur_j - g.nbc, t & 1);
-      if (km != 0xffffffffu) {
+      if (km_cur != 0xffffffffu) {
+        // this lane's rows, shifted so each row's bit sits at a compile-time position
+        const uint32_t kml = km_cur >> (4 * (lane >> 5));
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const int krow = 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-          if (!((km >> krow) & 1u)) {
+          if (!((kml >> (8 * (e >> 2) + (e & 3))) & 1u)) {
             st[0][e] = -INFINITY;
             st[1][e] = -INFINITY;
           }
@@ -151,6 +161,9 @@ __device__ __forceinline__ void attend_span(const Geom& g, const bf16x8* __restr
     const int pn = tn >> 1;
     const int nxt_j = irow[pn + (pn >= p_split ? p_skip : 0)];
     const int noff = nxt_j * cube_bytes + (tn & 1) * (32 * D * 2);
+    // the next tile's slot mask is requested a whole tile ahead of its use
+    uint32_t km_nxt = ~0u;
+    if constexpr (RAGGED) km_nxt = key_half_mask(kmask, nxt_j, tn & 1);
     if constexpr (EARLY_K) {
       // ---- request next tile's K now (longer lead, more live registers) ----
 #pragma unroll
@@ -212,6 +225,7 @@ __device__ __forceinline__ void attend_span(const Geom& g, const bf16x8* __restr
 #pragma unroll
     for (int u = 0; u < DB * 2; ++u) vr[u] = bld16(rv, vlane, noff + u * 1024);
     cur_j = nxt_j;
+    km_cur = km_nxt;
   }
 }
 
@@ -230,7 +244,7 @@ template <int D, bool EARLY_K, bool RAGGED>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_mfma_kernel(
     Geom g, const bf16_t* __restrict__ q_row, const bf16_t* __restrict__ krow,
     const bf16_t* __restrict__ vtr, const int32_t* __restrict__ idx, int k_sel, float c_log2,
-    int cpx, bf16_t* __restrict__ o, float* __restrict__ lse) {
+    int cpx, const uint2* __restrict__ kmask, bf16_t* __restrict__ o, float* __restrict__ lse) {
   constexpr int DB = D / 32;
   constexpr int cube_bytes = 64 * D * 2;
   __shared__ bf16x8 qs[(D / 16) * 2 * 64];
@@ -254,8 +268,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   zero_acc<D>(acc);
   float m_run[2] = {-INFINITY, -INFINITY};
   float l_part[2] = {0.f, 0.f};
-  attend_span<D, EARLY_K, RAGGED>(g, qs, rk, rv, irow, 0, 2 * k_sel, k_sel, 0, c_log2, lane, acc, m_run,
-                          l_part);
+  attend_span<D, EARLY_K, RAGGED>(g, qs, rk, rv, irow, 0, 2 * k_sel, k_sel, 0, c_log2, kmask,
+                                  lane, acc, m_run, l_part);
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     const float l = l_part[qb] + __shfl_xor(l_part[qb], 32, 64);
@@ -289,7 +303,8 @@ template <int D, bool EARLY_K, bool RAGGED>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_split_kernel(
     Geom g, const bf16_t* __restrict__ q_row, const bf16_t* __restrict__ krow,
     const bf16_t* __restrict__ vtr, const int32_t* __restrict__ idx, int k_sel, float c_log2,
-    int ns, int rcc, int rcn, bf16_t* __restrict__ o_part, float2* __restrict__ ml_part) {
+    int ns, int rcc, int rcn, const uint2* __restrict__ kmask, bf16_t* __restrict__ o_part,
+    float2* __restrict__ ml_part) {
   constexpr int DB = D / 32;
   constexpr int cube_bytes = 64 * D * 2;
   __shared__ bf16x8 qs[(D / 16) * 2 * 64];
@@ -331,8 +346,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   zero_acc<D>(acc);
   float m_run[2] = {-INFINITY, -INFINITY};
   float l_part[2] = {0.f, 0.f};
-  attend_span<D, EARLY_K, RAGGED>(g, qs, rk, rv, irow, 2 * lo1, 2 * (lo1 + n_sel), hi1, lo2 - hi1, c_log2,
-                          lane, acc, m_run, l_part);
+  attend_span<D, EARLY_K, RAGGED>(g, qs, rk, rv, irow, 2 * lo1, 2 * (lo1 + n_sel), hi1,
+                                  lo2 - hi1, c_log2, kmask, lane, acc, m_run, l_part);
   bf16_t* op = o_part + item * (64 * D);
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
@@ -418,6 +433,8 @@ size_t fwd_split_bytes(const Geom& g, int ns) {
   return items * 64 * g.D * sizeof(bf16_t) + items * 64 * sizeof(float2) + 256;
 }
 
+size_t fwd_kmask_bytes(const Geom& g) { return g.ragged ? (size_t)g.nbk * sizeof(uint2) : 0; }
+
 int fwd_split_ranges(const Geom& g, int k_sel, int requested) {
   if (requested >= 0) return requested <= 1 ? 1 : requested;
   // Split when the noise cubes a query cube selects out of a head's noise K/V (32 KB per cube)
@@ -429,16 +446,32 @@ int fwd_split_ranges(const Geom& g, int k_sel, int requested) {
   return (head_kv > 8.0 * (1 << 20) && mostly_noise) ? 8 : 1;
 }
 
+// Slot masks of every key cube of a ragged grid, condition cubes first: word h of cube j has
+// bit k set iff slot 32*h + k of the 64-token cube holds a token.
+__global__ __launch_bounds__(256) void key_mask_kernel(Geom g, uint2* __restrict__ kmask) {
+  const int j = blockIdx.x * 256 + threadIdx.x;
+  if (j >= g.nbk) return;
+  const int jc = j < g.nbc ? j : j - g.nbc;  // cube index inside its segment
+  kmask[j] = make_uint2(cube_half_mask(g, jc, 0), cube_half_mask(g, jc, 1));
+}
+
 template <int D, bool EK, bool RG>
 static hipError_t launch_fwd_t(const Geom& g, const bf16_t* q_row, const bf16_t* k_row,
                                const bf16_t* v_trans, const int32_t* idx, int k_sel,
                                float c_log2, void* o, float* lse, int ns, void* split_ws,
-                               hipStream_t s) {
+                               uint2* kmask, hipStream_t s) {
+  if constexpr (RG) {
+    // slot masks of every key cube, once per call (the tile loop only loads them)
+    hipLaunchKernelGGL(key_mask_kernel, dim3((unsigned)((g.nbk + 255) / 256)), dim3(256), 0, s, g,
+                       kmask);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   if (ns <= 1) {
     const int cpx = (g.nbq + 7) / 8;
     dim3 grid((unsigned)(g.B * g.Hh * cpx * 8));
     hipLaunchKernelGGL((fwd_mfma_kernel<D, EK, RG>), grid, dim3(64), 0, s, g, q_row,
-                       k_row, v_trans, idx, k_sel, c_log2, cpx, (bf16_t*)o, lse);
+                       k_row, v_trans, idx, k_sel, c_log2, cpx, kmask, (bf16_t*)o, lse);
     return hipGetLastError();
   }
   const int rcc = (g.nbc + ns - 1) / ns;
@@ -449,7 +482,7 @@ static hipError_t launch_fwd_t(const Geom& g, const bf16_t* q_row, const bf16_t*
   const int passes = (ns + 7) / 8;
   dim3 grid((unsigned)(8 * passes * g.B * g.Hh * g.nbq));
   hipLaunchKernelGGL((fwd_split_kernel<D, EK, RG>), grid, dim3(64), 0, s, g, q_row,
-                     k_row, v_trans, idx, k_sel, c_log2, ns, rcc, rcn, o_part, ml_part);
+                     k_row, v_trans, idx, k_sel, c_log2, ns, rcc, rcn, kmask, o_part, ml_part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   dim3 mgrid(g.nbq, g.B * g.Hh);
@@ -460,7 +493,8 @@ static hipError_t launch_fwd_t(const Geom& g, const bf16_t* q_row, const bf16_t*
 
 hipError_t launch_fwd_mfma(const Geom& g, const bf16_t* q_row, const bf16_t* k_row,
                            const bf16_t* v_trans, const int32_t* idx, int k_sel, float scale,
-                           void* o, float* lse, int ns, void* split_ws, hipStream_t s) {
+                           void* o, float* lse, int ns, void* split_ws, uint2* kmask,
+                           hipStream_t s) {
   const float c_log2 = scale * kLog2e;
   // Next-K request right after the S MFMAs needs ~30 more VGPRs; D = 128 has no room for them
   // at two waves per SIMD, so there it is requested together with V (tuning override:
@@ -469,9 +503,9 @@ hipError_t launch_fwd_mfma(const Geom& g, const bf16_t* q_row, const bf16_t* k_r
   const bool early = env ? std::atoi(env) != 0 : g.D == 64;
 #define BSA_FWD_CALL(DD, EK)                                                                   \
   (g.ragged ? launch_fwd_t<DD, EK, true>(g, q_row, k_row, v_trans, idx, k_sel, c_log2, o, lse, \
-                                         ns, split_ws, s)                                        \
+                                         ns, split_ws, kmask, s)                                 \
             : launch_fwd_t<DD, EK, false>(g, q_row, k_row, v_trans, idx, k_sel, c_log2, o, lse, \
-                                          ns, split_ws, s))
+                                          ns, split_ws, kmask, s))
   hipError_t e;
   if (g.D == 64)
     e = early ? BSA_FWD_CALL(64, true) : BSA_FWD_CALL(64, false);
