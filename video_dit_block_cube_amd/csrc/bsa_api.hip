@@ -110,7 +110,7 @@ Geom noise_only(const Geom& g) {
 }
 
 struct BwdWs {
-  size_t delta, lse, ld, bits, off, list, g_qr, g_dr, g_kr, g_vr, total;
+  size_t delta, lse, ld, bits, off, list, g_qr, g_dr, g_kr, g_vr, order, total;
 };
 
 BwdWs bwd_layout(const Geom& g, bool mfma, int k_sel) {
@@ -135,6 +135,7 @@ BwdWs bwd_layout(const Geom& g, bool mfma, int k_sel) {
     w.g_dr = take(gq);
     w.g_kr = take(gk);
     w.g_vr = take(gk);
+    w.order = take(dkdv_order_bytes(g));
   }
   w.total = at;
   return w;
@@ -356,9 +357,14 @@ bsa_status_t bsa_sparse_attn_bwd(const bsa_problem_t* p, bsa_dtype_t dtype, cons
                       "gather V");
       if (st != BSA_OK) return st;
       stages.done("gather_qkv_do");
+      // longest-first dK/dV dispatch; BSA_DKDV_ORDER=0 keeps the fixed order (tuning aid)
+      const char* ord_env = std::getenv("BSA_DKDV_ORDER");
+      int32_t* order = (ord_env && std::atoi(ord_env) == 0)
+                           ? nullptr
+                           : reinterpret_cast<int32_t*>(base + w.order);
       st = hip_status(launch_bwd_dkdv_mfma(g, at(w.g_kr), at(w.g_vr), at(w.g_qr), at(w.g_dr),
-                                           ld_c, off, list, softmax_scale, dk, dv, dk_cache,
-                                           dv_cache, stream),
+                                           ld_c, off, list, order, softmax_scale, dk, dv,
+                                           dk_cache, dv_cache, stream),
                       "dK/dV launch");
       if (st != BSA_OK) return st;
       stages.done("bwd_dkdv_mfma");

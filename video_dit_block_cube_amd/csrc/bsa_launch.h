@@ -79,10 +79,13 @@ hipError_t launch_bwd_dq_mfma(const Geom& g, const bf16_t* q_row, const bf16_t* 
                               const bf16_t* k_row, const bf16_t* v_row, const float2* ld_c,
                               const int32_t* idx, int k_sel, float scale, float* dq,
                               hipStream_t s);
+// order: dkdv_order_bytes(g) bytes the launch fills with the longest-first item order (null:
+// the fixed XCD-balanced order).
+size_t dkdv_order_bytes(const Geom& g);
 hipError_t launch_bwd_dkdv_mfma(const Geom& g, const bf16_t* k_row, const bf16_t* v_row,
                                 const bf16_t* q_row, const bf16_t* do_row, const float2* ld_c,
-                                const int32_t* csr_off, const int32_t* csr_list, float scale,
-                                float* dk, float* dv, float* dk_cache, float* dv_cache,
-                                hipStream_t s);
+                                const int32_t* csr_off, const int32_t* csr_list, int32_t* order,
+                                float scale, float* dk, float* dv, float* dk_cache,
+                                float* dv_cache, hipStream_t s);
 
 }  // namespace bsa

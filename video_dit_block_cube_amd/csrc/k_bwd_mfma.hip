@@ -26,14 +26,84 @@ namespace bsa {
 // accumulators are the B operands of dV^T += dO^T P and dK^T += Q^T dS, whose A operands are
 // read transposed from the same staged rows.
 // ---------------------------------------------------------------------------------------------
+// XCD x takes the x-th run of ccx condition cube ids and the x-th run of ncx noise cube ids of
+// every (b, h), condition cubes (whose lists hold every query cube) first, so the XCDs carry
+// equal work.  Slot k8 of XCD x -> (bh, key cube j: condition cubes first, then noise cubes);
+// false for a slot past the last cube.
+__device__ __forceinline__ bool dkdv_identity_item(const Geom& g, int x, int k8, int ccx, int ncx,
+                                                   int& bh, int& j) {
+  const int per = ccx + ncx;
+  bh = k8 / per;
+  const int m = k8 % per;
+  if (m < ccx) {
+    j = x * ccx + m;
+    return j < g.nbc;
+  }
+  j = x * ncx + (m - ccx);
+  if (j >= g.nbq) return false;
+  j += g.nbc;
+  return true;
+}
+
+constexpr int kOrderBuckets = 256;
+
+// Longest-first dispatch order of the dK/dV items inside each (b, h): a key cube's item takes
+// time in proportion to its list length (the query cubes that selected it), which varies about
+// +-16% around k_sel on these workloads and up to 1.5x.  The (b, h) groups keep their sequence,
+// so the items running together on an XCD still share one head's Q/dO rows in the Infinity
+// Cache (sorting across heads made dK/dV 9% slower).  Workgroup (x, bh) sorts XCD x's slots of
+// bh into buckets of list length (width 2^shift), longest first, and writes them to
+// order[8*(bh*per + pos) + x]; its slots past the item count get -1.  Items of one bucket land
+// in atomic (run-dependent) order, which changes nothing in any item's arithmetic.
+__global__ __launch_bounds__(256) void dkdv_order_kernel(Geom g,
+                                                         const int32_t* __restrict__ csr_off,
+                                                         int ccx, int ncx, int shift,
+                                                         int32_t* __restrict__ order) {
+  __shared__ int cnt[kOrderBuckets];
+  __shared__ int total;
+  const int x = blockIdx.x, bh = blockIdx.y;
+  const int per = ccx + ncx;
+  for (int i = threadIdx.x; i < kOrderBuckets; i += 256) cnt[i] = 0;
+  __syncthreads();
+  const int32_t* o = csr_off + (size_t)bh * (g.nbk + 1);
+  auto bucket = [&](int j) {
+    const int b = (o[j + 1] - o[j]) >> shift;
+    return kOrderBuckets - 1 - (b < kOrderBuckets - 1 ? b : kOrderBuckets - 1);
+  };
+  for (int m = threadIdx.x; m < per; m += 256) {
+    int bh2, j;
+    if (dkdv_identity_item(g, x, bh * per + m, ccx, ncx, bh2, j)) atomicAdd(&cnt[bucket(j)], 1);
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int sum = 0;
+    for (int i = 0; i < kOrderBuckets; ++i) {
+      const int c = cnt[i];
+      cnt[i] = sum;
+      sum += c;
+    }
+    total = sum;
+  }
+  __syncthreads();
+  const size_t base = (size_t)bh * per;
+  for (int m = threadIdx.x; m < per; m += 256) {
+    int bh2, j;
+    if (dkdv_identity_item(g, x, bh * per + m, ccx, ncx, bh2, j)) {
+      const int pos = atomicAdd(&cnt[bucket(j)], 1);
+      order[8 * (base + pos) + x] = bh * g.nbk + j;
+    }
+  }
+  for (int k = total + threadIdx.x; k < per; k += 256) order[8 * (base + k) + x] = -1;
+}
+
 template <int D>
 __global__ __launch_bounds__(64) void bwd_dkdv_mfma_kernel(
     Geom g, const bf16_t* __restrict__ k_row, const bf16_t* __restrict__ v_row,
     const bf16_t* __restrict__ q_row, const bf16_t* __restrict__ do_row,
     const float2* __restrict__ ld_c, const int32_t* __restrict__ csr_off,
-    const int32_t* __restrict__ csr_list, float scale, float c_log2, int ccx, int ncx,
-    float* __restrict__ dk, float* __restrict__ dv, float* __restrict__ dk_cache,
-    float* __restrict__ dv_cache) {
+    const int32_t* __restrict__ csr_list, const int32_t* __restrict__ order, float scale,
+    float c_log2, int ccx, int ncx, float* __restrict__ dk, float* __restrict__ dv,
+    float* __restrict__ dk_cache, float* __restrict__ dv_cache) {
   constexpr int S = D / 16;
   constexpr int DB = D / 32;
   constexpr int cube_bytes = 64 * D * 2;
@@ -42,19 +112,17 @@ __global__ __launch_bounds__(64) void bwd_dkdv_mfma_kernel(
   __shared__ __attribute__((aligned(16))) char stage0[stage_bytes];
   __shared__ __attribute__((aligned(16))) char stage1[stage_bytes];
 
-  const int L = blockIdx.x;
-  const int xcd = L & 7;
-  const int k8 = L >> 3;
-  // XCD x takes the x-th run of ccx condition cube ids and the x-th run of ncx noise cube ids
-  // of every (b, h), condition cubes (whose lists hold every query cube) first, so the XCDs
-  // carry equal work and the long items start early.
-  const int per = ccx + ncx;
-  const int bh = k8 / per;
-  const int m = k8 % per;
-  const bool cube_ok = m < ccx ? xcd * ccx + m < g.nbc : xcd * ncx + (m - ccx) < g.nbq;
-  if (!cube_ok) return;
-  // key cube id: condition cubes first, then noise cubes
-  const int j = m < ccx ? xcd * ccx + m : g.nbc + xcd * ncx + (m - ccx);
+  // Work item (b*Hh + h, key cube j) of workgroup L, which runs on XCD L % 8.
+  int bh, j;
+  if (order) {
+    // longest lists first inside each XCD's share (dkdv_order_kernel); -1: idle slot
+    const int it = order[blockIdx.x];
+    if (it < 0) return;
+    bh = it / g.nbk;
+    j = it % g.nbk;
+  } else if (!dkdv_identity_item(g, blockIdx.x & 7, blockIdx.x >> 3, ccx, ncx, bh, j)) {
+    return;
+  }
   const int b = bh / g.Hh, h = bh % g.Hh;
   const int lane = threadIdx.x;
   const int l32 = lane & 31;
@@ -211,21 +279,34 @@ __global__ __launch_bounds__(64) void bwd_dkdv_mfma_kernel(
 }
 
 
+size_t dkdv_order_bytes(const Geom& g) {
+  const int ccx = (g.nbc + 7) / 8, ncx = (g.nbq + 7) / 8;
+  return (size_t)g.B * g.Hh * (ccx + ncx) * 8 * sizeof(int32_t);
+}
+
 hipError_t launch_bwd_dkdv_mfma(const Geom& g, const bf16_t* k_row, const bf16_t* v_row,
                                 const bf16_t* q_row, const bf16_t* do_row, const float2* ld_c,
-                                const int32_t* csr_off, const int32_t* csr_list, float scale,
-                                float* dk, float* dv, float* dk_cache, float* dv_cache,
-                                hipStream_t s) {
+                                const int32_t* csr_off, const int32_t* csr_list, int32_t* order,
+                                float scale, float* dk, float* dv, float* dk_cache,
+                                float* dv_cache, hipStream_t s) {
   const int ccx = (g.nbc + 7) / 8, ncx = (g.nbq + 7) / 8;
   dim3 grid((unsigned)(g.B * g.Hh * (ccx + ncx) * 8));
   const float c_log2 = scale * kLog2e;
+  if (order) {
+    int shift = 0;  // list lengths are at most nbq: fit them into the buckets
+    while ((g.nbq >> shift) >= kOrderBuckets - 1) ++shift;
+    hipLaunchKernelGGL(dkdv_order_kernel, dim3(8, (unsigned)(g.B * g.Hh)), dim3(256), 0, s, g,
+                       csr_off, ccx, ncx, shift, order);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   if (g.D == 64)
     hipLaunchKernelGGL(bwd_dkdv_mfma_kernel<64>, grid, dim3(64), 0, s, g, k_row, v_row, q_row,
-                       do_row, ld_c, csr_off, csr_list, scale, c_log2, ccx, ncx, dk, dv,
+                       do_row, ld_c, csr_off, csr_list, order, scale, c_log2, ccx, ncx, dk, dv,
                        dk_cache, dv_cache);
   else
     hipLaunchKernelGGL(bwd_dkdv_mfma_kernel<128>, grid, dim3(64), 0, s, g, k_row, v_row, q_row,
-                       do_row, ld_c, csr_off, csr_list, scale, c_log2, ccx, ncx, dk, dv,
+                       do_row, ld_c, csr_off, csr_list, order, scale, c_log2, ccx, ncx, dk, dv,
                        dk_cache, dv_cache);
   return hipGetLastError();
 }
