@@ -47,8 +47,12 @@ def test_max_noise_cubes_sampled():
     assert exact >= len(cubes) - 2
     ks, scale = orc.num_selected(op, w.r), scale_of(op)
     o, lse = bsa.bsa_sparse_attn_fwd(p, t["q"], t["k"], t["v"], idx_d, ks, scale)
+    # dK/dV start as NaN: every key cube's work item (ordered longest-first inside the head) must
+    # write its rows, zeros for a cube no query selected
+    import torch
+    nan = lambda: torch.full(t["q"].shape, float("nan"), dtype=torch.float32, device=t["q"].device)
     dq, dk, dv = bsa.bsa_sparse_attn_bwd(p, t["q"], t["k"], t["v"], o, t["dO"], lse, idx_d, ks,
-                                         scale)
+                                         scale, dk=nan(), dv=nan())
     rows = [(0, 0, int(i)) for i in cubes[:8]]
     ref = orc.attn_fwd_rows(x["q"], x["k"], x["v"], None, None, idx, op, scale, rows)
     toks = orc.noise_cube_tokens(op)
@@ -61,6 +65,13 @@ def test_max_noise_cubes_sampled():
         assert_close(dq[b, toks[i], h], rq[(b, h, i)], "bf16", f"dQ cube {i}")
     for a in (dk, dv):
         assert bool(torch_isfinite(a))
+    counts = np.bincount(idx[0, 0].ravel(), minlength=op.nbk)
+    cols = [(0, 0, int(j)) for j in (int(np.argmax(counts)), int(np.argmin(counts)), *cubes[2:5])]
+    _, rk, rv = orc.attn_bwd(x["q"], x["k"], x["v"], x["dO"], idx, op, scale, key_cubes=cols)[:3]
+    dk, dv = dk.cpu().numpy(), dv.cpu().numpy()
+    for (b, h, j) in cols:
+        assert_close(dk[b, toks[j], h], rk[(b, h, j)], "bf16", f"dK cube {j} ({counts[j]} queries)")
+        assert_close(dv[b, toks[j], h], rv[(b, h, j)], "bf16", f"dV cube {j}")
 
 
 def torch_isfinite(a):
@@ -87,8 +98,12 @@ def test_largest_cube_256_tokens(number, dtype):
     idx_d = torch.from_numpy(np.ascontiguousarray(idx, dtype=np.int32)).to("cuda:0")
     ks, scale = orc.num_selected(op, w.r), scale_of(op)
     o, lse = bsa.bsa_sparse_attn_fwd(p, t["q"], t["k"], t["v"], idx_d, ks, scale)
+    # dK/dV start as NaN: every key cube's work item (ordered longest-first inside the head) must
+    # write its rows, zeros for a cube no query selected
+    import torch
+    nan = lambda: torch.full(t["q"].shape, float("nan"), dtype=torch.float32, device=t["q"].device)
     dq, dk, dv = bsa.bsa_sparse_attn_bwd(p, t["q"], t["k"], t["v"], o, t["dO"], lse, idx_d, ks,
-                                         scale)
+                                         scale, dk=nan(), dv=nan())
     O, LSE = orc.sparse_attn_fwd(x["q"], x["k"], x["v"], None, None, idx, op, scale)
     assert_close(o.float().cpu().numpy(), O, w.dtype, "O")
     ref = orc.attn_bwd(x["q"], x["k"], x["v"], dO, idx, op, scale)
