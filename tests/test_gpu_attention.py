@@ -271,11 +271,16 @@ def test_bwd_720p_full_size_sampled():
     ks = orc.num_selected(op, w.r)
     scale = scale_of(op)
     o, lse = bsa.bsa_sparse_attn_fwd(p, t["q"], t["k"], t["v"], idx_d, ks, scale)
+    # gradients start as NaN: every query and key cube of every head must be written
+    import torch
+    nan = lambda: torch.full(t["q"].shape, float("nan"), dtype=torch.float32, device=t["q"].device)
     dq, dk, dv = bsa.bsa_sparse_attn_bwd(p, t["q"], t["k"], t["v"], o, t["dO"], lse, idx_d, ks,
-                                         scale)
+                                         scale, dq=nan(), dk=nan(), dv=nan())
     del t, o, lse
     idx = idx_d.cpu().numpy()
     dq, dk, dv = (a.cpu().numpy() for a in (dq, dk, dv))
+    for name, a in (("dQ", dq), ("dK", dk), ("dV", dv)):
+        assert np.isfinite(a).all(), f"{name}: unwritten (NaN) entries"
     rows = sample_rows(op, [0, 17, 31], 3, seed=21)
     cols = sample_rows(op, [0, 17, 31], 3, seed=22)
     rq, rk, rv = orc.attn_bwd(x["q"], x["k"], x["v"], x["dO"], idx, op, scale, rows=rows,
