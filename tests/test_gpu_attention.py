@@ -168,8 +168,13 @@ def test_fwd_full_size_sampled(number):
     idx_d = _gpu_selection(w, t, p)
     ks = orc.num_selected(op, w.r)
     scale = scale_of(op)
+    # outputs start as NaN, so "finite everywhere" below also proves every entry was written
+    import torch
+    o0 = torch.full_like(t["q"], float("nan"))
+    l0 = torch.full((p.batch, p.heads, p.Nq), float("nan"), dtype=torch.float32,
+                    device=t["q"].device)
     o, lse = bsa.bsa_sparse_attn_fwd(p, t["q"], t["k"], t["v"], idx_d, ks, scale,
-                                     t.get("k_cache"), t.get("v_cache"))
+                                     t.get("k_cache"), t.get("v_cache"), o=o0, lse=l0)
     idx = idx_d.cpu().numpy()
     o = o.float().cpu().numpy()
     lse = lse.cpu().numpy()

@@ -158,9 +158,18 @@ def test_real_720p_latent_grid_sampled():
     km = bsa.bsa_block_pool(p, t["k"])
     idx_d, _ = bsa.bsa_select_topr(p, qm, km, w.r, with_mask=False)
     ks, scale = orc.num_selected(op, w.r), scale_of(op)
-    o, lse = bsa.bsa_sparse_attn_fwd(p, t["q"], t["k"], t["v"], idx_d, ks, scale)
+    # outputs start as NaN: every token, those of the partial edge cubes included, must be written
+    import torch
+    nan = lambda dt=torch.float32: torch.full(t["q"].shape, float("nan"), dtype=dt,
+                                              device=t["q"].device)
+    l0 = torch.full((p.batch, p.heads, p.Nq), float("nan"), dtype=torch.float32,
+                    device=t["q"].device)
+    o, lse = bsa.bsa_sparse_attn_fwd(p, t["q"], t["k"], t["v"], idx_d, ks, scale,
+                                     o=nan(t["q"].dtype), lse=l0)
     dq, dk, dv = bsa.bsa_sparse_attn_bwd(p, t["q"], t["k"], t["v"], o, t["dO"], lse, idx_d, ks,
-                                         scale)
+                                         scale, dq=nan(), dk=nan(), dv=nan())
+    for name, a in (("O", o), ("LSE", lse), ("dQ", dq), ("dK", dk), ("dV", dv)):
+        assert bool(torch.isfinite(a).all()), f"{name}: unwritten (NaN) entries"
     idx = idx_d.cpu().numpy()
     o, dq = o.float().cpu().numpy(), dq.cpu().numpy()
     gw = 20
