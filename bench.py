@@ -135,6 +135,8 @@ def main() -> int:
                     help="skip the dense-attention (r = all) forward comparison")
     ap.add_argument("--no-480p", action="store_true",
                     help="skip the 480p-class forward + backward step")
+    ap.add_argument("--no-d64", action="store_true",
+                    help="skip the 720p-class forward + backward step at head dim 64")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -269,7 +271,10 @@ def main() -> int:
     }
 
     if not args.no_480p:
-        out["step_480p"] = bench_480p(bsa, synth, torch, dev)
+        out["step_480p"] = bench_step(bsa, synth, torch, dev, 5, "480p-class")
+    if not args.no_d64:
+        log("720p-class step at head dim 64")
+        out["step_720p_d64"] = bench_step(bsa, synth, torch, dev, 3, "720p-class", head_dim=64)
     if not args.no_continuation:
         out["continuation_fwd"] = bench_continuation(bsa, synth, orc, torch, dev, args)
     if not args.no_dense:
@@ -392,11 +397,11 @@ def _time_fwd(bsa, torch, p, t, r, reps=3):
     return ks, float(np.median(tot))
 
 
-def bench_480p(bsa, synth, torch, dev, reps=5):
-    """The headline step (pool x2, select, forward, backward) at the 480p-class grid 24x32x52
-    (QKNorm q/k, top-r = 62, dO ~ N(0,1)): per-call ms from HIP events on the launch stream."""
+def bench_step(bsa, synth, torch, dev, number, label, reps=5, **over):
+    """The headline step (pool x2, select, forward, backward) on another seeded workload (QKNorm
+    q/k, dO ~ N(0,1)): per-call ms from HIP events on the launch stream."""
     import numpy as np
-    w = synth.workload(5)
+    w = synth.workload(number, with_grad=True, **over)
     log(f"drawing inputs for {w.name}")
     x = synth.make_inputs(w)
     t = {k: torch.from_numpy(v).to(dev).to(torch.bfloat16) for k, v in x.items()}
@@ -448,8 +453,9 @@ def bench_480p(bsa, synth, torch, dev, reps=5):
                                             "bwd_dq_mfma"))
     step_ms = sum(med.values())
     f = fwd_flops(p, ks)
-    return {"workload": "480p-class BSA fwd+bwd: B=1, Hh=32, D=128, grid 24x32x52, cube 4x4x4, "
-                        "top-r=62 + own cube, QKNorm q/k, dO~N(0,1)",
+    return {"workload": f"{label} BSA fwd+bwd: B={w.batch}, Hh={w.heads}, D={w.head_dim}, grid "
+                        f"{w.T}x{w.H}x{w.W}, cube {w.cube_t}x{w.cube_h}x{w.cube_w}, top-r={w.r} "
+                        "+ own cube, QKNorm q/k, dO~N(0,1)",
             "k_sel": ks, "fwd_tflop": round(f / 1e12, 3),
             "step_ms": round(step_ms, 3), "fwd_ms": round(fwd_ms, 3), "bwd_ms": round(bwd_ms, 3),
             "value_tflops": round(3.5 * f / (step_ms * 1e-3) / 1e12, 1),

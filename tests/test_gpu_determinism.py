@@ -31,6 +31,7 @@ def _run(p, t, r, ks, scale):
     (5, (("heads", 4),), None),                                  # 480p grid, default 8-range split
     (4, (("heads", 2), ("T", 12), ("H", 24), ("W", 40), ("cond_T", 4)), None),  # continuation
     (5, (("heads", 2), ("H", 30), ("W", 50)), "16"),             # ragged grid, 16 ranges
+    (5, (("heads", 4), ("head_dim", 64)), None),                 # D = 64: 16-query dK/dV steps
 ])
 def test_bit_identical_reruns(number, over, splits, monkeypatch):
     if splits is not None:

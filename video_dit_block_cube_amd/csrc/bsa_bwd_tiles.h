@@ -73,6 +73,64 @@ __device__ __forceinline__ bf16x8 lds_trans_frag(const lds_char* stage, int lane
   return __builtin_bit_cast(bf16x8, both);
 }
 
+// ---------------------------------------------------------------------------------------------
+// 16-row steps on v_mfma_f32_16x16x32_bf16 (A: lane = row 16-block position, 8 consecutive k at
+// 8*(lane/16); D: lane holds rows 4*(lane/16) + i of column lane%16).
+// ---------------------------------------------------------------------------------------------
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+
+// Byte offset inside a ROW half block of the 16-byte fragment holding row r0 + lane%16, columns
+// 32*s + 8*(lane/16) .. +7: lane part and (s, r0) part.
+__device__ __forceinline__ int row16_lane(int lane) { return ((lane >> 4) * 64 + (lane & 15)) * 16; }
+template <int D>
+__device__ __forceinline__ int row16_const(int s, int r0) {
+  return ((((32 * s) % (D / 2)) / 8) * 64 + ((32 * s) / (D / 2)) * 32 + r0) * 16;
+}
+
+// Transposed read (ds_read_b64_tr_b16) of the 16-row block `sub` of a staged half: lane gets
+// rows 16*sub + 8*(lane/32) + 0..7, in natural order, of column 32*db + lane%32 (the same
+// pointing rule as lds_trans_frag with the row index 8*(g/2) + 4*eh + n/4).
+__device__ __forceinline__ int tr16_lane(int lane) {
+  const int g = lane >> 4, n = lane & 15;
+  return ((128 * (g & 1) + 64 * ((n & 3) >> 1) + 8 * (g >> 1) + (n >> 2)) * 8 + 4 * (n & 1)) * 2;
+}
+template <int D>
+__device__ __forceinline__ int tr16_const(int db, int sub, int eh) {
+  if constexpr (D == 128) return ((256 * (db & 1) + 32 * (db >> 1) + 16 * sub + 4 * eh) * 8) * 2;
+  else return ((32 * db + 16 * sub + 4 * eh) * 8) * 2;  // D == 64
+}
+template <int D>
+__device__ __forceinline__ bf16x8 lds_tr16(const lds_char* stage, int lane_base, int db, int sub) {
+  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4i16*)(stage + lane_base + tr16_const<D>(db, sub, 0)));
+  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4i16*)(stage + lane_base + tr16_const<D>(db, sub, 1)));
+  typedef short v8i16 __attribute__((ext_vector_type(8)));
+  const v8i16 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, both);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// Two 16x16 accumulators x, y of key blocks 2kb, 2kb+1 (lane: query 4*(lane/16) + i, key
+// lane%16 of its block) -> the bf16 B operand of a 32x32x16 product over those 16 queries (lane:
+// key 32kb + lane%32, queries 8*(lane/32) + 0..7).  v_permlane16_swap exchanges the odd 16-lane
+// rows of the first register with the even rows of the second, which moves every lane's missing
+// four queries of its key in from the neighbouring row.
+__device__ __forceinline__ bf16x8 acc16_to_b32(const f32x4v& x, const f32x4v& y) {
+  const auto s0 = __builtin_amdgcn_permlane16_swap(pack_bf16x2(x[0], x[1]), pack_bf16x2(y[0], y[1]),
+                                                   false, false);
+  const auto s1 = __builtin_amdgcn_permlane16_swap(pack_bf16x2(x[2], x[3]), pack_bf16x2(y[2], y[3]),
+                                                   false, false);
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = {s0[0], s1[0], s0[1], s1[1]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
 // One 32-row half block (S*1 KB) of a ROW-gathered tensor -> LDS, no VGPRs in between.
 template <int D>
 __device__ __forceinline__ void stage_half(__amdgpu_buffer_rsrc_t r, int soff, lds_char* dst,
