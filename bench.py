@@ -135,6 +135,8 @@ def main() -> int:
                     help="skip the dense-attention (r = all) forward comparison")
     ap.add_argument("--no-480p", action="store_true",
                     help="skip the 480p-class forward + backward step")
+    ap.add_argument("--no-smooth", action="store_true",
+                    help="skip the 720p-class step on spatially smooth Q/K")
     ap.add_argument("--no-d64", action="store_true",
                     help="skip the 720p-class forward + backward step at head dim 64")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -272,6 +274,9 @@ def main() -> int:
 
     if not args.no_480p:
         out["step_480p"] = bench_step(bsa, synth, torch, dev, 5, "480p-class")
+    if not args.no_smooth:
+        log("720p-class step on spatially smooth Q/K")
+        out["smooth_qk_720p"] = bench_smooth(bsa, synth, torch, dev)
     if not args.no_d64:
         log("720p-class step at head dim 64")
         out["step_720p_d64"] = bench_step(bsa, synth, torch, dev, 3, "720p-class", head_dim=64)
@@ -526,6 +531,89 @@ def bench_ragged(bsa, synth, torch, dev, args, reps=3):
             # per step (pool runs twice)
             "stages_ms_per_step": {k: round(float(np.sum(v)) / reps, 4) for k, v in stage_ms.items()},
             "note": "pool x2, select, fwd, bwd; partial edge cubes masked in the kernels"}
+
+
+def bench_smooth(bsa, synth, torch, dev, reps=3):
+    """The headline step on spatially smooth Q/K (not one of the configs): real video tokens are
+    similar to their neighbours, so neighbouring query cubes select overlapping key cubes, where
+    the N(0,1) configs select uniformly at random (no K/V reuse between neighbours).  Q and K
+    are trilinear upsamplings of noise drawn on a (T/2, H/8, W/8) grid, plus 0.3x white noise,
+    RMS-normalised per head; V and dO stay N(0,1)."""
+    import numpy as np
+    import torch.nn.functional as F
+    w = synth.workload(3, with_grad=True)
+    p = bsa.Problem(**w.shape_dict)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(8080)
+    C = p.heads * p.head_dim
+
+    def smooth():
+        lo = torch.randn((1, C, p.T // 2, p.H // 8, p.W // 8), generator=gen, device=dev)
+        x = F.interpolate(lo, size=(p.T, p.H, p.W), mode="trilinear", align_corners=False)
+        x = x.permute(0, 2, 3, 4, 1).reshape(1, p.Nq, p.heads, p.head_dim)
+        x = x + 0.3 * torch.randn(x.shape, generator=gen, device=dev)
+        x = x / torch.sqrt(x.square().mean(dim=-1, keepdim=True) + 1e-6)
+        return x.to(torch.bfloat16).contiguous()
+
+    t = {"q": smooth(), "k": smooth()}
+    for n in ("v", "dO"):
+        t[n] = torch.randn((1, p.Nq, p.heads, p.head_dim), generator=gen, device=dev).to(
+            torch.bfloat16)
+    ks = bsa.bsa_num_selected(p, w.r)
+    scale = 1.0 / math.sqrt(p.head_dim)
+    wsf = torch.empty(bsa.bsa_workspace_bytes(p, torch.bfloat16, ks, False), dtype=torch.uint8,
+                      device=dev)
+    wsb = torch.empty(bsa.bsa_workspace_bytes(p, torch.bfloat16, ks, True), dtype=torch.uint8,
+                      device=dev)
+    qm = torch.empty((p.batch, p.heads, p.nbq, p.head_dim), dtype=torch.float32, device=dev)
+    km = torch.empty_like(qm)
+    idx = torch.empty((p.batch, p.heads, p.nbq, ks), dtype=torch.int32, device=dev)
+    o = torch.empty_like(t["q"])
+    lse = torch.empty((p.batch, p.heads, p.Nq), dtype=torch.float32, device=dev)
+    dq, dk, dv = (torch.empty(t["q"].shape, dtype=torch.float32, device=dev) for _ in range(3))
+
+    def step(ev):
+        calls = [lambda: bsa.bsa_block_pool(p, t["q"], qm),
+                 lambda: bsa.bsa_block_pool(p, t["k"], km),
+                 lambda: bsa.bsa_select_topr(p, qm, km, w.r, with_mask=False, idx=idx),
+                 lambda: bsa.bsa_sparse_attn_fwd(p, t["q"], t["k"], t["v"], idx, ks, scale, o=o,
+                                                 lse=lse, workspace=wsf),
+                 lambda: bsa.bsa_sparse_attn_bwd(p, t["q"], t["k"], t["v"], o, t["dO"], lse, idx,
+                                                 ks, scale, dq=dq, dk=dk, dv=dv, workspace=wsb)]
+        for e, c in zip(ev, calls):
+            with e:
+                c()
+
+    step([bsa.StageEvents(8) for _ in range(5)])
+    torch.cuda.synchronize()
+    evs = [[bsa.StageEvents(8) for _ in range(5)] for _ in range(reps)]
+    for ev in evs:
+        step(ev)
+    torch.cuda.synchronize()
+    stage: dict = {}
+    for ev in evs:
+        per = {}
+        for e in ev:
+            for name, ms in e.elapsed_all():
+                per[name] = per.get(name, 0.0) + ms
+        for name, ms in per.items():
+            stage.setdefault(name, []).append(ms)
+    med = {k: float(np.median(v)) for k, v in stage.items()}
+    step_ms = sum(med.values())
+    # locality of the selection: share of a query cube's selected key cubes that its raster
+    # neighbour (next cube along w) also selected, averaged over heads 0 and 31
+    sel = idx.cpu().numpy()
+    share = []
+    for h in (0, p.heads - 1):
+        a, b = sel[0, h, :-1], sel[0, h, 1:]
+        share.append(np.mean([len(np.intersect1d(x, y)) / ks for x, y in zip(a, b)]))
+    f = fwd_flops(p, ks)
+    return {"workload": "720p-class grid and selection size on smooth Q/K (correlated over "
+                        "about 2x2 cubes in h and w), V and dO ~ N(0,1)",
+            "neighbour_selection_overlap": round(float(np.mean(share)), 3),
+            "step_ms": round(step_ms, 3),
+            "value_tflops": round(3.5 * f / (step_ms * 1e-3) / 1e12, 1),
+            "stages_ms_per_step": {k: round(v, 4) for k, v in med.items()}}
 
 
 def bench_prologue(bsa, torch, dev, p, reps=5):
