@@ -29,6 +29,7 @@ if ROOT not in sys.path:
 METRIC = "BSA fwd+bwd effective TFLOP/s & % bf16 MFMA peak; ms/call at 720p-class grid"
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
+PEAK_CLOCK_GHZ = 2.4            # the clock the bf16 peak is quoted at
 
 
 def log(msg: str) -> None:
@@ -62,12 +63,12 @@ def stage_bytes(name: str, p, k_sel: int) -> float | None:
             "bwd_prep": 2 * tensor + 4 * per_query + 2 * idx}.get(name)
 
 
-def traffic_from_profile(stage: str):
-    """HBM bytes per launch measured by rocprofv3 counters (profiles/traffic_<stage>.txt), or None
-    when no measurement exists or the kernel source changed since it was taken."""
+def profile_record(stage: str) -> dict:
+    """Counter results of a kernel (profiles/traffic_<stage>.txt: HBM bytes per launch, shader
+    clock), or {} when no measurement exists or the kernel source changed since it was taken."""
     path = os.path.join(ROOT, "profiles", f"traffic_{stage}.txt")
     if not os.path.exists(path):
-        return None
+        return {}
     kv = {}
     for line in open(path):
         if ":" in line and not line.startswith("#"):
@@ -76,16 +77,19 @@ def traffic_from_profile(stage: str):
     # "source" lists the kernel's files (comma separated); the hash covers their bytes in order
     srcs = [os.path.join(ROOT, f.strip()) for f in kv.get("source", "").split(",") if f.strip()]
     if not srcs or not all(os.path.exists(f) for f in srcs):
-        return None
+        return {}
     h = hashlib.sha256()
     for f in srcs:
         h.update(open(f, "rb").read())
     if h.hexdigest() != kv.get("source_sha256"):
-        return None
-    try:
-        return float(kv["hbm_bytes_per_launch"])
-    except (KeyError, ValueError):
-        return None
+        return {}
+    rec = {}
+    for key in ("hbm_bytes_per_launch", "clock_ghz"):
+        try:
+            rec[key] = float(kv[key])
+        except (KeyError, ValueError):
+            pass
+    return rec
 
 
 def cpu_baseline(x, op, idx, r, budget_s: float = 12.0):
@@ -231,11 +235,17 @@ def main() -> int:
     dominant = max((k for k in avg if kernel_flops(k, p, ks)), key=lambda k: avg[k])
     dom_flops = kernel_flops(dominant, p, ks)
     achieved = dom_flops / (avg[dominant] * 1e-3) / 1e12
+    rec = profile_record(dominant)
     roofline = {"bound": "mfma", "kernel": dominant, "achieved": round(achieved, 2),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                "traffic": traffic_from_profile(dominant),
+                "traffic": rec.get("hbm_bytes_per_launch"),
                 "flops_per_launch": dom_flops, "avg_launch_ms": round(avg[dominant], 4)}
+    if "clock_ghz" in rec:
+        # the same MFMA peak at the clock the kernel actually ran at (power-limited)
+        pk = PEAK_BF16_TFLOPS * rec["clock_ghz"] / PEAK_CLOCK_GHZ
+        roofline.update(clock_ghz=rec["clock_ghz"], peak_at_clock=round(pk, 1),
+                        frac_at_clock=round(achieved / pk, 4))
     per_kernel = {}
     for k, v in avg.items():
         kf = kernel_flops(k, p, ks)
