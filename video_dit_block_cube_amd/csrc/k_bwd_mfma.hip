@@ -12,6 +12,8 @@
 // back with ds_read_b64_tr_b16, so each tile crosses the fabric once.  The next tile is requested
 // as soon as the current one is staged; per-lane byte offsets stay constant and the wave-uniform
 // tile offset rides in an SGPR (buffer loads).
+#include <type_traits>
+
 #include "bsa_bwd_tiles.h"
 
 namespace bsa {
@@ -350,6 +352,203 @@ __global__ __launch_bounds__(64) void bwd_dkdv_mfma_kernel(
 }
 
 
+// ---------------------------------------------------------------------------------------------
+// dK, dV at D = 128 with two waves per key cube.  The accumulators of one 64-key cube (dV^T and
+// dK^T, 128 registers each) hold a single wave at one wave per SIMD, where its softmax VALU,
+// LDS reads and MFMAs serialise.  Split by output instead: wave 0 holds K and accumulates dV,
+// wave 1 holds V and accumulates dK, each within 256 registers, so two waves share every SIMD
+// and overlap each other's VALU and MFMA work.  Per 16-query sub-step (16x16x32 products, as
+// in the D = 64 path of the one-wave kernel):
+//   wave 0: S = Q K^T, P = exp2(S*scale*log2e - LSE2) -> bf16 P to LDS; barrier; dV^T += dO^T P
+//   wave 1: dP = dO V^T; barrier; dS = P o (dP - Delta) with the bf16 P; dK^T += Q^T dS
+// Wave 0 stages the Q rows and wave 1 the dO rows of every 32-query half (each with its own
+// copy of the (LSE2, Delta) pairs), so each reads its own rows before the barrier; the next
+// half is requested right after the first barrier of a step, when both waves are past the
+// previous step.  The roles run separate copies of the loop with the same barrier sequence.
+// ---------------------------------------------------------------------------------------------
+__device__ __forceinline__ void pair_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS writes are done (no vmcnt
+                                       // wait: the next half's LDS-bound loads stay in flight)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <int D>
+__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) void
+bwd_dkdv_pair_kernel(Geom g, const bf16_t* __restrict__ k_row, const bf16_t* __restrict__ v_row,
+                     const bf16_t* __restrict__ q_row, const bf16_t* __restrict__ do_row,
+                     const float2* __restrict__ ld_c, const int32_t* __restrict__ csr_off,
+                     const int32_t* __restrict__ csr_list, const int32_t* __restrict__ order,
+                     float scale, float c_log2, int ccx, int ncx, float* __restrict__ dk,
+                     float* __restrict__ dv, float* __restrict__ dk_cache,
+                     float* __restrict__ dv_cache) {
+  constexpr int S4 = D / 32;
+  constexpr int DB = D / 32;
+  constexpr int cube_bytes = 64 * D * 2;
+  constexpr int half_bytes = 32 * D * 2;
+  constexpr int stage_bytes = 2 * half_bytes + 512;  // Q | dO | pairs (wave 0) | pairs (wave 1)
+  __shared__ __attribute__((aligned(16))) char stage0[stage_bytes];
+  __shared__ __attribute__((aligned(16))) char stage1[stage_bytes];
+  __shared__ __attribute__((aligned(16))) char xch[2][16 * 64 * 2];  // bf16 P of a sub-step
+
+  int bh, j;
+  if (order) {
+    const int it = order[blockIdx.x];
+    if (it < 0) return;
+    bh = it / g.nbk;
+    j = it % g.nbk;
+  } else if (!dkdv_identity_item(g, blockIdx.x & 7, blockIdx.x >> 3, ccx, ncx, bh, j)) {
+    return;
+  }
+  const int b = bh / g.Hh, h = bh % g.Hh;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // 0: K, dV   1: V, dK
+  const int lane = threadIdx.x & 63;
+  const int l32 = lane & 31, hh = lane >> 5;
+
+  const int32_t* offs = csr_off + (size_t)bh * (g.nbk + 1);
+  const int beg = offs[j], end = offs[j + 1];
+  const int nsteps = 2 * (end - beg);
+  const size_t bh_bytes = (size_t)g.nbq * cube_bytes;
+  const size_t bh_elems = (size_t)g.nbq * 64 * D;
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc((wave ? do_row : q_row) + bh * bh_elems, bh_bytes);
+  const __amdgpu_buffer_rsrc_t rl =
+      make_rsrc(ld_c + (size_t)bh * g.nbq * 64, (size_t)g.nbq * 64 * sizeof(float2));
+  lds_char* st0 = (lds_char*)stage0;
+  lds_char* st1 = (lds_char*)stage1;
+  const int own_rows = wave * half_bytes;             // this wave's rows inside a stage
+  const int own_pairs = 2 * half_bytes + 256 * wave;  // this wave's (LSE2, Delta) pairs
+  auto stage_step = [&](int i, int qb, lds_char* dst) {
+    stage_half<D>(rs, i * cube_bytes + qb * half_bytes, dst + own_rows, lane);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rl, (__attribute__((address_space(3))) void*)(dst + own_pairs), 4, lane * 4,
+        (i * 64 + 32 * qb) * (int)sizeof(float2), 0, 0);
+  };
+  if (nsteps > 0) stage_step(csr_list[beg], 0, st0);
+
+  // K (wave 0) or V (wave 1) rows of the key cube: B operands of the 16x16x32 products,
+  // kv[nb*S4 + s] = (lane%16 = key of 16-block nb, d = 32s + 8*(lane/16) + 0..7)
+  const size_t kv_elems = (size_t)g.nbk * 64 * D;
+  const __amdgpu_buffer_rsrc_t rkv =
+      make_rsrc((wave ? v_row : k_row) + bh * kv_elems, (size_t)g.nbk * cube_bytes);
+  const int r16 = row16_lane(lane);
+  bf16x8 kv[4 * S4];
+#pragma unroll
+  for (int f = 0; f < 4 * S4; ++f) {
+    const int nb = f / S4, s = f % S4;
+    kv[f] = bld16(rkv, r16,
+                  j * cube_bytes + (nb >> 1) * half_bytes + row16_const<D>(s, 16 * (nb & 1)));
+  }
+  f32x16 acc[DB][2];  // dV^T (wave 0) or dK^T (wave 1)
+#pragma unroll
+  for (int db = 0; db < DB; ++db) { zero16(acc[db][0]); zero16(acc[db][1]); }
+  const int trb = tr16_lane(lane);
+
+  auto step = [&](int t, lds_char* cur, lds_char* nxt, auto role_c) {
+    constexpr int R = decltype(role_c)::value;
+    const int tn = t + 1 < nsteps ? t + 1 : t;  // the last step re-stages itself
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's rows of the half have landed
+    const __attribute__((address_space(3))) float2* ldp =
+        (const __attribute__((address_space(3))) float2*)(cur + own_pairs);
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      f32x4v sc[4];
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) sc[nb] = f32x4v{0.f, 0.f, 0.f, 0.f};
+      // S = Q K^T (wave 0) or dP = dO V^T (wave 1), from the wave's own staged rows
+#pragma unroll
+      for (int s = 0; s < S4; ++s) {
+        const bf16x8 a = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(
+            cur + own_rows + r16 + row16_const<D>(s, 16 * sub));
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb)
+          sc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, kv[nb * S4 + s], sc[nb], 0, 0, 0);
+      }
+      __attribute__((address_space(3))) uint32_t* x =
+          (__attribute__((address_space(3))) uint32_t*)(xch[sub]) + lane * 8;
+      const int q0 = 16 * sub + 4 * (lane >> 4);  // this lane's first query of the sub-step
+      if constexpr (R == 0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float lv = ldp[q0 + i].x;
+#pragma unroll
+          for (int nb = 0; nb < 4; ++nb) sc[nb][i] = fast_exp2(fmaf(sc[nb][i], c_log2, -lv));
+        }
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+          x[2 * nb] = pack_bf16x2(sc[nb][0], sc[nb][1]);
+          x[2 * nb + 1] = pack_bf16x2(sc[nb][2], sc[nb][3]);
+        }
+        bf16x8 pb[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) pb[kb] = acc16_to_b32(sc[2 * kb], sc[2 * kb + 1]);
+        pair_barrier();  // P is in LDS; both waves have finished the previous step
+        if (sub == 0) stage_step(csr_list[beg + (tn >> 1)], tn & 1, nxt);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const bf16x8 dt = lds_tr16<D>(cur + half_bytes, trb, db, sub);
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb) acc[db][kb] = mfma32(dt, pb[kb], acc[db][kb]);
+        }
+      } else {
+        pair_barrier();
+        if (sub == 0) stage_step(csr_list[beg + (tn >> 1)], tn & 1, nxt);
+        // dS = P o (dP - Delta) from wave 0's bf16 P (same lane layout as this accumulator)
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+          const uint32_t w0 = x[2 * nb], w1 = x[2 * nb + 1];
+          const float pv[4] = {__uint_as_float(w0 << 16), __uint_as_float(w0 & 0xffff0000u),
+                               __uint_as_float(w1 << 16), __uint_as_float(w1 & 0xffff0000u)};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sc[nb][i] = pv[i] * (sc[nb][i] - ldp[q0 + i].y);
+        }
+        bf16x8 dsb[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) dsb[kb] = acc16_to_b32(sc[2 * kb], sc[2 * kb + 1]);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const bf16x8 qt = lds_tr16<D>(cur, trb, db, sub);
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb) acc[db][kb] = mfma32(qt, dsb[kb], acc[db][kb]);
+        }
+      }
+    }
+  };
+  // nsteps is even; fixed stage roles per pair of steps (see the one-wave kernel)
+  if (wave == 0) {
+    for (int t = 0; t < nsteps; t += 2) {
+      step(t, st0, st1, std::integral_constant<int, 0>{});
+      step(t + 1, st1, st0, std::integral_constant<int, 0>{});
+    }
+  } else {
+    for (int t = 0; t < nsteps; t += 2) {
+      step(t, st0, st1, std::integral_constant<int, 1>{});
+      step(t + 1, st1, st0, std::integral_constant<int, 1>{});
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the last re-staging has landed
+
+  const bool cond = j < g.nbc;  // condition key cube: its gradients go to the cache tensors
+  float* out = wave ? (cond ? dk_cache : dk) : (cond ? dv_cache : dv);
+  const float mul = wave ? scale : 1.0f;
+  const int jc = cond ? j : j - g.nbc;  // cube index inside its segment
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    const int tk = cube_token(g, jc, 32 * kb + l32);
+    if (tk < 0) continue;  // slot outside a ragged grid
+    const size_t off = bnhd_offset(g, cond ? g.Nc : g.Nq, b, tk, h);
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int d = 32 * db + 8 * r4 + 4 * hh;
+        const f32x16& a = acc[db][kb];
+        *reinterpret_cast<float4*>(out + off + d) = make_float4(
+            a[4 * r4] * mul, a[4 * r4 + 1] * mul, a[4 * r4 + 2] * mul, a[4 * r4 + 3] * mul);
+      }
+  }
+}
+
 size_t dkdv_order_bytes(const Geom& g) {
   const int ccx = (g.nbc + 7) / 8, ncx = (g.nbq + 7) / 8;
   return (size_t)g.B * g.Hh * (ccx + ncx) * 8 * sizeof(int32_t);
@@ -376,7 +575,7 @@ hipError_t launch_bwd_dkdv_mfma(const Geom& g, const bf16_t* k_row, const bf16_t
                        do_row, ld_c, csr_off, csr_list, order, scale, c_log2, ccx, ncx, dk, dv,
                        dk_cache, dv_cache);
   else
-    hipLaunchKernelGGL(bwd_dkdv_mfma_kernel<128>, grid, dim3(64), 0, s, g, k_row, v_row, q_row,
+    hipLaunchKernelGGL(bwd_dkdv_pair_kernel<128>, grid, dim3(128), 0, s, g, k_row, v_row, q_row,
                        do_row, ld_c, csr_off, csr_list, order, scale, c_log2, ccx, ncx, dk, dv,
                        dk_cache, dv_cache);
   return hipGetLastError();
