@@ -6,12 +6,12 @@
 //   dV_j += P^T dO_i,  dS = P o (dO_i V_j^T - Delta_i),  dQ_i += scale*dS K_j,
 //   dK_j += scale*dS^T Q_i.
 //
-// MI355X design: two kernels (dQ here and dK/dV), each owning its output in registers so no fp32
-// atomics are needed.  Every operand comes from the ROW gather layout; the streamed operand's
-// rows are staged straight into LDS with buffer_load ... lds and its transposed uses are read
-// back with ds_read_b64_tr_b16, so each tile crosses the fabric once.  The next tile is requested
-// as soon as the current one is staged; per-lane byte offsets stay constant and the wave-uniform
-// tile offset rides in an SGPR (buffer loads).
+// MI355X design: the backward is two passes (dK/dV here, dQ in k_bwd_dq.hip), each owning its
+// output in registers so no fp32 atomics are needed.  Every operand comes from the ROW gather
+// layout; the streamed operand's rows are staged straight into LDS with buffer_load ... lds and
+// their transposed uses are read back with ds_read_b64_tr_b16, so each tile crosses the fabric
+// once.  Per-lane byte offsets stay constant and the wave-uniform tile offset rides in an SGPR
+// (buffer loads).
 #include <type_traits>
 
 #include "bsa_bwd_tiles.h"
@@ -19,14 +19,16 @@
 namespace bsa {
 
 // ---------------------------------------------------------------------------------------------
-// dK, dV (key-stationary over the CSR transpose): grid = B*Hh*(ccx+ncx)*8, one wave per key cube
-// (condition cubes, read from the cache and written to the cache gradients, and noise cubes).
-// K and V rows of the key cube are B operands held
-// in registers; per 32-query half of each query cube that selected j, the Q and dO rows are staged
-// straight into LDS (double buffered), S = Q K^T and dP = dO V^T read them as A operands (each
-// row fragment read once and applied to both 32-key halves), and P, dS built in place in the
-// accumulators are the B operands of dV^T += dO^T P and dK^T += Q^T dS, whose A operands are
-// read transposed from the same staged rows.
+// dK, dV (key-stationary over the CSR transpose): grid = B*Hh*(ccx+ncx)*8 work items, one per key
+// cube (condition cubes, read from the cache and written to the cache gradients, and noise
+// cubes), longest lists first within each (b, h).  For every query cube that selected the key
+// cube, the Q and dO rows of each 32-query half are staged straight into LDS (double buffered);
+// S = Q K^T and dP = dO V^T take them as A operands against the key cube's K and V rows held in
+// registers, and P, dS are the B operands of dV^T += dO^T P and dK^T += Q^T dS, whose A operands
+// are read transposed from the same staged rows.  Two kernels:
+//   bwd_dkdv_mfma_kernel (D = 64): one wave per key cube, 16-query sub-steps (248 registers,
+//     two waves per SIMD);
+//   bwd_dkdv_pair_kernel (D = 128): two waves per key cube split by output (below).
 // ---------------------------------------------------------------------------------------------
 // XCD x takes the x-th run of ccx condition cube ids and the x-th run of ncx noise cube ids of
 // every (b, h), condition cubes (whose lists hold every query cube) first, so the XCDs carry
@@ -106,6 +108,7 @@ __global__ __launch_bounds__(64) void bwd_dkdv_mfma_kernel(
     const int32_t* __restrict__ csr_list, const int32_t* __restrict__ order, float scale,
     float c_log2, int ccx, int ncx, float* __restrict__ dk, float* __restrict__ dv,
     float* __restrict__ dk_cache, float* __restrict__ dv_cache) {
+  static_assert(D == 64, "D = 128 runs bwd_dkdv_pair_kernel");
   constexpr int S = D / 16;
   constexpr int DB = D / 32;
   constexpr int cube_bytes = 64 * D * 2;
@@ -152,30 +155,21 @@ __global__ __launch_bounds__(64) void bwd_dkdv_mfma_kernel(
   };
   if (nsteps > 0) stage_step(csr_list[beg], 0, st0);
 
-  // K and V rows of this key cube as B operands; the K/V gathers hold every key cube (condition
-  // cubes from the cache first).  D = 128: 32x32x16 layout, kreg[kb*S + s] = (lane = key of half
-  // kb, 8 consecutive d of step s).  D = 64: 16x16x32 layout (16-query steps, below),
+  // K and V rows of this key cube as B operands of the 16x16x32 products; the K/V gathers hold
+  // every key cube (condition cubes from the cache first).
   // kreg[nb*S4 + s] = (lane%16 = key of 16-block nb, d = 32s + 8*(lane/16) + 0..7).
-  constexpr bool Q16 = D == 64;
   constexpr int S4 = D / 32;
   const size_t kv_elems = (size_t)g.nbk * 64 * D;
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(k_row + bh * kv_elems, (size_t)g.nbk * cube_bytes);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(v_row + bh * kv_elems, (size_t)g.nbk * cube_bytes);
   const int r16 = row16_lane(lane);
-  bf16x8 kreg[2 * S], vreg[2 * S];
+  bf16x8 kreg[4 * S4], vreg[4 * S4];
 #pragma unroll
-  for (int f = 0; f < 2 * S; ++f) {
-    int voff, soff;
-    if constexpr (Q16) {
-      const int nb = f / S4, s = f % S4;
-      voff = r16;
-      soff = j * cube_bytes + (nb >> 1) * half_bytes + row16_const<D>(s, 16 * (nb & 1));
-    } else {
-      voff = lane * 16;
-      soff = j * cube_bytes + f * 1024;  // f = kb*S + s
-    }
-    kreg[f] = bld16(rk, voff, soff);
-    vreg[f] = bld16(rv, voff, soff);
+  for (int f = 0; f < 4 * S4; ++f) {
+    const int nb = f / S4, s = f % S4;
+    const int soff = j * cube_bytes + (nb >> 1) * half_bytes + row16_const<D>(s, 16 * (nb & 1));
+    kreg[f] = bld16(rk, r16, soff);
+    vreg[f] = bld16(rv, r16, soff);
   }
 
   f32x16 acck[DB][2], accv[DB][2];
@@ -183,7 +177,7 @@ __global__ __launch_bounds__(64) void bwd_dkdv_mfma_kernel(
   for (int db = 0; db < DB; ++db)
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) { zero16(acck[db][kb]); zero16(accv[db][kb]); }
-  const int trb = Q16 ? tr16_lane(lane) : tr_lane_base(lane);
+  const int trb = tr16_lane(lane);
 
   auto step = [&](int t, lds_char* cur, lds_char* nxt) {
     const int tn = t + 1 < nsteps ? t + 1 : t;
@@ -191,130 +185,59 @@ __global__ __launch_bounds__(64) void bwd_dkdv_mfma_kernel(
     __builtin_amdgcn_s_waitcnt(0x0f70 | ((2 * S + 1) & 0xf) | (((2 * S + 1) >> 4) << 14));
     const __attribute__((address_space(3))) f32x4* ldp =
         (const __attribute__((address_space(3))) f32x4*)(cur + 2 * half_bytes);
-    if constexpr (Q16) {
-      // 16-query steps (D = 64): S and dP of 16 queries x 64 keys on 16x16x32 MFMAs (four key
-      // blocks), P and dS moved into the 32x32x16 B-operand layout by permlane swaps; the fewer
-      // live accumulators keep the kernel within 256 registers, two waves per SIMD.
+    // two 16-query sub-steps per staged half
 #pragma unroll
-      for (int sub = 0; sub < 2; ++sub) {
-        f32x4v sc[4], dp[4];
+    for (int sub = 0; sub < 2; ++sub) {
+      f32x4v sc[4], dp[4];
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb) {
-          sc[nb] = f32x4v{0.f, 0.f, 0.f, 0.f};
-          dp[nb] = sc[nb];
-        }
+      for (int nb = 0; nb < 4; ++nb) {
+        sc[nb] = f32x4v{0.f, 0.f, 0.f, 0.f};
+        dp[nb] = sc[nb];
+      }
 #pragma unroll
-        for (int s = 0; s < S4; ++s) {
-          const bf16x8 a = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(
-              cur + r16 + row16_const<D>(s, 16 * sub));
-#pragma unroll
-          for (int nb = 0; nb < 4; ++nb)
-            sc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, kreg[nb * S4 + s], sc[nb], 0, 0, 0);
-        }
-        // (base-2 LSE, Delta) of this lane's queries 16*sub + 4*(lane/16) + 0..3
-        const f32x4 p01 = ldp[8 * sub + 2 * (lane >> 4)];
-        const f32x4 p23 = ldp[8 * sub + 2 * (lane >> 4) + 1];
-        const float lv[4] = {p01[0], p01[2], p23[0], p23[2]};
-        const float dl[4] = {p01[1], p01[3], p23[1], p23[3]};
+      for (int s = 0; s < S4; ++s) {
+        const bf16x8 a = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(
+            cur + r16 + row16_const<D>(s, 16 * sub));
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb)
+          sc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, kreg[nb * S4 + s], sc[nb], 0, 0, 0);
+      }
+      // (base-2 LSE, Delta) of this lane's queries 16*sub + 4*(lane/16) + 0..3
+      const f32x4 p01 = ldp[8 * sub + 2 * (lane >> 4)];
+      const f32x4 p23 = ldp[8 * sub + 2 * (lane >> 4) + 1];
+      const float lv[4] = {p01[0], p01[2], p23[0], p23[2]};
+      const float dl[4] = {p01[1], p01[3], p23[1], p23[3]};
 #pragma unroll
-          for (int i = 0; i < 4; ++i) sc[nb][i] = fast_exp2(fmaf(sc[nb][i], c_log2, -lv[i]));
-        bf16x8 pb[2], dsb[2];
+      for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) pb[kb] = acc16_to_b32(sc[2 * kb], sc[2 * kb + 1]);
+        for (int i = 0; i < 4; ++i) sc[nb][i] = fast_exp2(fmaf(sc[nb][i], c_log2, -lv[i]));
+      bf16x8 pb[2], dsb[2];
 #pragma unroll
-        for (int s = 0; s < S4; ++s) {
-          const bf16x8 a = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(
-              cur + half_bytes + r16 + row16_const<D>(s, 16 * sub));
+      for (int kb = 0; kb < 2; ++kb) pb[kb] = acc16_to_b32(sc[2 * kb], sc[2 * kb + 1]);
 #pragma unroll
-          for (int nb = 0; nb < 4; ++nb)
-            dp[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, vreg[nb * S4 + s], dp[nb], 0, 0, 0);
-        }
+      for (int s = 0; s < S4; ++s) {
+        const bf16x8 a = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(
+            cur + half_bytes + r16 + row16_const<D>(s, 16 * sub));
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb)
+          dp[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, vreg[nb * S4 + s], dp[nb], 0, 0, 0);
+      }
 #pragma unroll
-          for (int i = 0; i < 4; ++i) dp[nb][i] = sc[nb][i] * (dp[nb][i] - dl[i]);
+      for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) dsb[kb] = acc16_to_b32(dp[2 * kb], dp[2 * kb + 1]);
+        for (int i = 0; i < 4; ++i) dp[nb][i] = sc[nb][i] * (dp[nb][i] - dl[i]);
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const bf16x8 dt = lds_tr16<D>(cur + half_bytes, trb, db, sub);
-          const bf16x8 qt = lds_tr16<D>(cur, trb, db, sub);
+      for (int kb = 0; kb < 2; ++kb) dsb[kb] = acc16_to_b32(dp[2 * kb], dp[2 * kb + 1]);
 #pragma unroll
-          for (int kb = 0; kb < 2; ++kb) {
-            accv[db][kb] = mfma32(dt, pb[kb], accv[db][kb]);
-            acck[db][kb] = mfma32(qt, dsb[kb], acck[db][kb]);
-          }
+      for (int db = 0; db < DB; ++db) {
+        const bf16x8 dt = lds_tr16<D>(cur + half_bytes, trb, db, sub);
+        const bf16x8 qt = lds_tr16<D>(cur, trb, db, sub);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          accv[db][kb] = mfma32(dt, pb[kb], accv[db][kb]);
+          acck[db][kb] = mfma32(qt, dsb[kb], acck[db][kb]);
         }
       }
-    } else {
-      // S = Q K^T for both key halves: each staged Q row fragment is read once
-      f32x16 sc[2];
-      zero16(sc[0]);
-      zero16(sc[1]);
-#pragma unroll
-      for (int s = 0; s < S; ++s) {
-        const bf16x8 a = lds_row_frag(cur, lane, s);
-        sc[0] = mfma32(a, kreg[s], sc[0]);
-        sc[1] = mfma32(a, kreg[S + s], sc[1]);
-      }
-      // P = exp2(S*scale*log2(e) - LSE2) in place (rows 8*r4 + 4*hh + e4 of the half per lane),
-      // with its bf16 copy as the B operand of dV^T; the exponentials overlap dP's MFMAs
-      bf16x8 pb[2][2], dsb[2][2];
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const f32x4 p01 = ldp[(8 * r4 + 4 * hh) / 2];
-        const f32x4 p23 = ldp[(8 * r4 + 4 * hh) / 2 + 1];
-        const float lv[4] = {p01[0], p01[2], p23[0], p23[2]};
-#pragma unroll
-        for (int e4 = 0; e4 < 4; ++e4) {
-          const int r = 4 * r4 + e4;
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb) {
-            const float p = fast_exp2(fmaf(sc[kb][r], c_log2, -lv[e4]));
-            sc[kb][r] = p;  // P in fp32 for dS
-            pb[kb][r >> 3][r & 7] = (__bf16)p;
-          }
-        }
-      }
-      // dP = dO V^T for both key halves, then dS = P o (dP - Delta)
-      f32x16 dp[2];
-      zero16(dp[0]);
-      zero16(dp[1]);
-#pragma unroll
-      for (int s = 0; s < S; ++s) {
-        const bf16x8 a = lds_row_frag(cur + half_bytes, lane, s);
-        dp[0] = mfma32(a, vreg[s], dp[0]);
-        dp[1] = mfma32(a, vreg[S + s], dp[1]);
-      }
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const f32x4 p01 = ldp[(8 * r4 + 4 * hh) / 2];
-        const f32x4 p23 = ldp[(8 * r4 + 4 * hh) / 2 + 1];
-        const float dv4[4] = {p01[1], p01[3], p23[1], p23[3]};
-#pragma unroll
-        for (int e4 = 0; e4 < 4; ++e4) {
-          const int r = 4 * r4 + e4;
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb) {
-            const float p = sc[kb][r];
-            dsb[kb][r >> 3][r & 7] = (__bf16)(p * (dp[kb][r] - dv4[e4]));
-          }
-        }
-      }
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-          const bf16x8 dt = lds_trans_frag<D>(cur + half_bytes, trb, db, s2);
-          const bf16x8 qt = lds_trans_frag<D>(cur, trb, db, s2);
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb) {
-            accv[db][kb] = mfma32(dt, pb[kb][s2], accv[db][kb]);
-            acck[db][kb] = mfma32(qt, dsb[kb][s2], acck[db][kb]);
-          }
-        }
     }
   };
   // nsteps is even (two 32-query halves per listed query cube); fixed stage roles per half let
