@@ -52,3 +52,29 @@ def test_bit_identical_reruns(number, over, splits, monkeypatch):
     for name, a, b in zip(names, first, second):
         assert a.dtype == b.dtype and a.shape == b.shape, name
         assert a.tobytes() == b.tobytes(), f"{name} differs between two identical calls"
+
+
+@pytest.mark.parametrize("number, over", [
+    (5, (("heads", 4),)),                                               # D = 128: two-wave dK/dV
+    (4, (("heads", 2), ("T", 12), ("H", 24), ("W", 40), ("cond_T", 4))),  # condition cubes
+    (5, (("heads", 2), ("head_dim", 64))),                              # D = 64: one-wave dK/dV
+])
+def test_dkdv_dispatch_order_changes_nothing(number, over, monkeypatch):
+    """dK/dV items run longest-first by default; the fixed id order (BSA_DKDV_ORDER=0) must give
+    the same bits, since no item's arithmetic depends on when it runs."""
+    w = synth.workload(number, **dict(over))
+    print_case(f"dK/dV dispatch order {w.name} {dict(over)}")
+    x = synth.make_inputs(w)
+    if "dO" not in x:
+        x["dO"] = synth.round_to_bf16(
+            np.random.default_rng(78).standard_normal(x["q"].shape).astype(np.float32))
+    p, op = bsa.Problem(**w.shape_dict), orc.Problem(**w.shape_dict)
+    t = {k: to_dev(v, w.dtype) for k, v in x.items()}
+    ks, scale = orc.num_selected(op, w.r), scale_of(op)
+    longest_first = _run(p, t, w.r, ks, scale)
+    monkeypatch.setenv("BSA_DKDV_ORDER", "0")
+    fixed = _run(p, t, w.r, ks, scale)
+    names = ["q_mean", "k_mean", "idx", "mask", "O", "LSE", "dQ", "dK", "dV", "dK_cache",
+             "dV_cache"]
+    for name, a, b in zip(names, longest_first, fixed):
+        assert a.tobytes() == b.tobytes(), f"{name} depends on the dK/dV dispatch order"
