@@ -163,6 +163,9 @@ bsa_status_t bsa_sparse_attn_fwd(const bsa_problem_t* p, bsa_dtype_t dtype, cons
  *   dk_cache, dv_cache device, [B, Nc, Hh, D] fp32, overwritten; NULL iff cond_T == 0
  *   ws, ws_bytes       device workspace of at least bsa_workspace_bytes(p, dtype, k_sel, 1)
  * With cond_T > 0 only the bf16 MFMA path (64-token cubes) is implemented: UNSUPPORTED otherwise.
+ * Precision (bf16): P and dS enter their products rounded to bf16, with fp32 accumulation; at
+ * head_dim 128 the dS of dK/dV is formed from the bf16-rounded P.  Results are deterministic
+ * (no atomics).
  * Errors: INVALID_ARG, SHAPE, UNSUPPORTED, WORKSPACE, HIP. */
 bsa_status_t bsa_sparse_attn_bwd(const bsa_problem_t* p, bsa_dtype_t dtype, const void* q,
                                  const void* k, const void* v, const void* k_cache,
