@@ -151,3 +151,24 @@ def test_pool_then_select_end_to_end(number):
                                   orc.block_pool(x["q"], op), orc.block_pool(x["k"], op), op,
                                   w.r, heads)
     assert ties <= 0.05 * (exact + ties)
+
+
+@pytest.mark.parametrize("T, H, W, D", [
+    (16, 64, 136, 128),   # 2176 cubes: the largest grid with 16 rows per workgroup at D = 128
+    (16, 64, 140, 128),   # 2240 cubes: 4 rows per workgroup
+    (16, 128, 128, 128),  # 4096 cubes: 2 rows per workgroup
+    (16, 64, 140, 64),    # 2240 cubes at D = 64: 16 rows per workgroup
+])
+def test_select_rows_per_workgroup_paths(T, H, W, D):
+    """The select kernel owns 16, 8, 4, 2 or 1 query rows per workgroup depending on how many
+    score rows fit in LDS; every path must give the oracle's selection bit for bit."""
+    w = synth.workload(2, heads=1, T=T, H=H, W=W, head_dim=D)
+    op = orc.Problem(**w.shape_dict)
+    print_case(f"select {op.nbq} cubes, D = {D}")
+    rng = np.random.default_rng(op.nbq + D)
+    qm = (rng.standard_normal((1, 1, op.nbq, D)) * 0.1).astype(np.float32)
+    km = (rng.standard_normal((1, 1, op.nbq, D)) * 0.1).astype(np.float32)
+    for r in (3, 144):
+        _, exact, ties = _select_pair(w, qm, km, r)
+        assert exact + ties == op.nbq
+        assert ties <= 0.05 * op.nbq
