@@ -78,3 +78,29 @@ def test_dkdv_dispatch_order_changes_nothing(number, over, monkeypatch):
              "dV_cache"]
     for name, a, b in zip(names, longest_first, fixed):
         assert a.tobytes() == b.tobytes(), f"{name} depends on the dK/dV dispatch order"
+
+
+@pytest.mark.parametrize("number, over", [
+    (5, (("heads", 4),)),                                               # D = 128: pipelined dQ
+    (4, (("heads", 2), ("T", 12), ("H", 24), ("W", 40), ("cond_T", 4))),  # condition cubes
+])
+def test_dq_pipeline_changes_nothing(number, over, monkeypatch):
+    """At head_dim 128 on grids without partial cubes dQ runs a software-pipelined loop; the plain
+    loop (BSA_DQ_PIPELINE=0) must give the same bits, since each tile's arithmetic and the order
+    of the dQ updates are the same."""
+    w = synth.workload(number, **dict(over))
+    print_case(f"dQ pipeline {w.name} {dict(over)}")
+    x = synth.make_inputs(w)
+    if "dO" not in x:
+        x["dO"] = synth.round_to_bf16(
+            np.random.default_rng(79).standard_normal(x["q"].shape).astype(np.float32))
+    p, op = bsa.Problem(**w.shape_dict), orc.Problem(**w.shape_dict)
+    t = {k: to_dev(v, w.dtype) for k, v in x.items()}
+    ks, scale = orc.num_selected(op, w.r), scale_of(op)
+    pipelined = _run(p, t, w.r, ks, scale)
+    monkeypatch.setenv("BSA_DQ_PIPELINE", "0")
+    plain = _run(p, t, w.r, ks, scale)
+    names = ["q_mean", "k_mean", "idx", "mask", "O", "LSE", "dQ", "dK", "dV", "dK_cache",
+             "dV_cache"]
+    for name, a, b in zip(names, pipelined, plain):
+        assert a.tobytes() == b.tobytes(), f"{name} differs between the dQ loops"

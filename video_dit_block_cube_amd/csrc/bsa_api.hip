@@ -368,8 +368,12 @@ bsa_status_t bsa_sparse_attn_bwd(const bsa_problem_t* p, bsa_dtype_t dtype, cons
                       "dK/dV launch");
       if (st != BSA_OK) return st;
       stages.done("bwd_dkdv_mfma");
+      // software-pipelined dQ where it is faster; BSA_DQ_PIPELINE=0 keeps the plain loop
+      // (same bits; tuning aid)
+      const char* pipe_env = std::getenv("BSA_DQ_PIPELINE");
+      const bool pipelined = !(pipe_env && std::atoi(pipe_env) == 0);
       st = hip_status(launch_bwd_dq_mfma(g, at(w.g_qr), at(w.g_dr), at(w.g_kr), at(w.g_vr),
-                                         ld_c, idx, k_sel, softmax_scale, dq, stream),
+                                         ld_c, idx, k_sel, softmax_scale, dq, pipelined, stream),
                       "dQ launch");
       stages.done("bwd_dq_mfma");
     } else {

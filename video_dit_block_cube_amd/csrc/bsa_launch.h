@@ -75,7 +75,13 @@ size_t fwd_kmask_bytes(const Geom& g);
 // LDS with ds_read_b64_tr_b16).
 // k_row / v_row cover all nbk key cubes (condition cubes first), q_row / do_row the nbq query
 // cubes; dK/dV of condition key cubes go to dk_cache / dv_cache ([B, Nc, Hh, D]).
+// pipelined: at D = 128 on a grid without partial cubes, run the software-pipelined variant
+// (same bits; launch_bwd_dq_pipe).
 hipError_t launch_bwd_dq_mfma(const Geom& g, const bf16_t* q_row, const bf16_t* do_row,
+                              const bf16_t* k_row, const bf16_t* v_row, const float2* ld_c,
+                              const int32_t* idx, int k_sel, float scale, float* dq,
+                              bool pipelined, hipStream_t s);
+hipError_t launch_bwd_dq_pipe(const Geom& g, const bf16_t* q_row, const bf16_t* do_row,
                               const bf16_t* k_row, const bf16_t* v_row, const float2* ld_c,
                               const int32_t* idx, int k_sel, float scale, float* dq,
                               hipStream_t s);

@@ -15,6 +15,8 @@
 //
 // This file is compiled with LLVM's register-minimising scheduler (build flags): it keeps the
 // score accumulators out of the AGPRs that hold dQ^T, which trims accumulator copies in the loop.
+// At head_dim 128 on grids whose sides are cube multiples the launcher runs the software-
+// pipelined variant (k_bwd_dq_pipe.hip) instead, which gives the same bits.
 #include "bsa_bwd_tiles.h"
 
 namespace bsa {
@@ -171,7 +173,9 @@ __global__ __launch_bounds__(64) void bwd_dq_mfma_kernel(
 hipError_t launch_bwd_dq_mfma(const Geom& g, const bf16_t* q_row, const bf16_t* do_row,
                               const bf16_t* k_row, const bf16_t* v_row, const float2* ld_c,
                               const int32_t* idx, int k_sel, float scale, float* dq,
-                              hipStream_t s) {
+                              bool pipelined, hipStream_t s) {
+  if (pipelined && g.D == 128 && !g.ragged)
+    return launch_bwd_dq_pipe(g, q_row, do_row, k_row, v_row, ld_c, idx, k_sel, scale, dq, s);
   const int cpx = (g.nbq + 7) / 8;
   dim3 grid((unsigned)(g.B * g.Hh * cpx * 8));
   const float c_log2 = scale * kLog2e;
