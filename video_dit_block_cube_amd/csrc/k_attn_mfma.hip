@@ -298,7 +298,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 // cube i) attends only the selected cubes of range s and writes a normalised partial O (bf16,
 // [64][D] row-major) plus its base-2 max and row sum.  Range s runs on XCD s%8, whose L2 then
 // only ever holds that range of the head's K/V; the XCD takes its ranges one after the other
-// (s = xcd, xcd + 8, ...), heads in order within each.
+// (s = xcd, xcd + 8, ...), heads in order within each.  A pass with r < 8 ranges deals range
+// x % r to XCD x, so every XCD works and the XCDs holding one range split its query cubes.
 template <int D, bool EARLY_K, bool RAGGED>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_split_kernel(
     Geom g, const bf16_t* __restrict__ q_row, const bf16_t* __restrict__ krow,
@@ -316,8 +317,16 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   const int rem = k8 % per_pass;
   const int bh = rem / g.nbq;
   const int i = rem % g.nbq;
-  const int sr = xcd + 8 * pass;
-  if (sr >= ns) return;
+  int sr = xcd + 8 * pass;
+  const int r_left = ns - 8 * pass;  // ranges in this pass
+  if (r_left < 8) {
+    // fewer ranges than XCDs: XCD x takes range x % r_left, and the c XCDs that share a range
+    // split its query cubes (cube i goes to the one with x / r_left == i % c)
+    const int s_in = xcd % r_left;
+    const int c = (8 - s_in + r_left - 1) / r_left;
+    if (i % c != xcd / r_left) return;
+    sr = 8 * pass + s_in;
+  }
   const int b = bh / g.Hh, h = bh % g.Hh;
   const int lane = threadIdx.x;
   const int l32 = lane & 31, hh = lane >> 5;
