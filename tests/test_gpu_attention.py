@@ -93,11 +93,12 @@ def test_fwd_continuation_small(path):
     assert_close(lse.cpu().numpy(), LSE, "bf16", "LSE", max_abs=2e-3, rel=1e-5)
 
 
-@pytest.mark.parametrize("splits, early", [(2, None), (3, None), (8, "1"), (16, "0"),
-                                           (40, None)])
+@pytest.mark.parametrize("splits, early", [(2, None), (3, None), (8, "1"), (11, None),
+                                           (16, "0"), (40, None)])
 def test_fwd_key_range_split(splits, early, monkeypatch):
     """The key-range split forward (partials + merge) against the oracle, including ranges that
-    hold no selected cube for some query cubes and more ranges than key cubes."""
+    hold no selected cube for some query cubes, more ranges than key cubes, and passes of fewer
+    than 8 ranges (2, 3, the last 3 of 11) whose XCDs share a range."""
     monkeypatch.setenv("BSA_FWD_SPLITS", str(splits))
     if early is not None:
         monkeypatch.setenv("BSA_FWD_EARLY_K", early)
