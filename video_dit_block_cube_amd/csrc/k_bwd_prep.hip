@@ -11,7 +11,9 @@
 // attention kernels read 64 contiguous floats per cube.  The transpose is deterministic and
 // atomic-free in global memory: (1) one workgroup per 32 query rows ORs the rows' bits into an
 // LDS word per key cube and writes the words column-major, (2) one workgroup per (b, h) popcounts
-// each column, scans the counts, and expands the set bits of each column in ascending row order.
+// each column and scans the counts into the list offsets, (3) one wave per key cube expands its
+// column's set bits in ascending row order (a wave prefix sum over the words' bit counts gives
+// each lane its first position).
 #include "bsa_launch.h"
 
 namespace bsa {
@@ -99,8 +101,7 @@ __global__ __launch_bounds__(256) void csr_bits_kernel(Geom g, const int32_t* __
 
 __global__ __launch_bounds__(1024) void csr_fill_kernel(Geom g, int k_sel,
                                                         const uint32_t* __restrict__ bits,
-                                                        int32_t* __restrict__ csr_off,
-                                                        int32_t* __restrict__ csr_list) {
+                                                        int32_t* __restrict__ csr_off) {
   extern __shared__ int32_t cnt[];  // [nbk] then [1024] thread totals
   int32_t* tot = cnt + g.nbk;
   const int bh = blockIdx.x;
@@ -130,21 +131,42 @@ __global__ __launch_bounds__(1024) void csr_fill_kernel(Geom g, int k_sel,
   int pre = tot[tid] - run;  // exclusive prefix of this segment
   int32_t* off_bh = csr_off + (size_t)bh * (g.nbk + 1);
   for (int j = lo; j < hi; ++j) {
-    const int c = cnt[j];
     off_bh[j] = (int32_t)(base + pre);
-    int pos = pre;
-    for (int w = 0; w < ngroups; ++w) {
-      uint32_t m = colbits[(size_t)j * ngroups + w];
-      while (m) {
-        const int bit = __ffs(m) - 1;
-        csr_list[base + pos] = w * 32 + bit;
-        ++pos;
-        m &= m - 1;
-      }
-    }
-    pre += c;
+    pre += cnt[j];
   }
   if (tid == 1023) off_bh[g.nbk] = (int32_t)(base + tot[1023]);
+}
+
+// One wave per key cube j: the query cubes whose bits are set in j's column, ascending, written
+// from csr_off[j] on.  Lane l expands word w0 + l of the column after a wave prefix sum of the
+// words' bit counts gives its first position.
+__global__ __launch_bounds__(1024) void csr_list_kernel(Geom g,
+                                                        const uint32_t* __restrict__ bits,
+                                                        const int32_t* __restrict__ csr_off,
+                                                        int32_t* __restrict__ csr_list) {
+  const int bh = blockIdx.y;
+  const int j = blockIdx.x * 16 + (threadIdx.x >> 6);
+  if (j >= g.nbk) return;
+  const int lane = threadIdx.x & 63;
+  const int ngroups = csr_groups(g);
+  const uint32_t* col = bits + ((size_t)bh * g.nbk + j) * ngroups;
+  int pos0 = csr_off[(size_t)bh * (g.nbk + 1) + j];
+  for (int w0 = 0; w0 < ngroups; w0 += 64) {
+    uint32_t m = (w0 + lane < ngroups) ? col[w0 + lane] : 0u;
+    const int c = __popc(m);
+    int incl = c;  // inclusive prefix over the lanes
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int t = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += t;
+    }
+    int pos = pos0 + incl - c;
+    while (m) {
+      csr_list[pos++] = (w0 + lane) * 32 + (__ffs(m) - 1);
+      m &= m - 1;
+    }
+    pos0 += __shfl(incl, 63, 64);
+  }
 }
 
 hipError_t launch_csr(const Geom& g, const int32_t* idx, int k_sel, uint32_t* bits,
@@ -162,7 +184,11 @@ hipError_t launch_csr(const Geom& g, const int32_t* idx, int k_sel, uint32_t* bi
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(csr_fill_kernel, dim3(g.B * g.Hh), dim3(1024), lds2, s, g, k_sel, bits,
-                     csr_off, csr_list);
+                     csr_off);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(csr_list_kernel, dim3((unsigned)((g.nbk + 15) / 16), g.B * g.Hh), dim3(1024),
+                     0, s, g, bits, csr_off, csr_list);
   return hipGetLastError();
 }
 
