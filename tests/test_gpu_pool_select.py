@@ -154,6 +154,7 @@ def test_pool_then_select_end_to_end(number):
 
 
 @pytest.mark.parametrize("T, H, W, D", [
+    (16, 40, 100, 128),   # 1000 cubes: 16 rows per workgroup, the last workgroup holds 8 rows
     (16, 64, 136, 128),   # 2176 cubes: the largest grid with 16 rows per workgroup at D = 128
     (16, 64, 140, 128),   # 2240 cubes: 4 rows per workgroup
     (16, 128, 128, 128),  # 4096 cubes: 2 rows per workgroup
