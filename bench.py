@@ -41,11 +41,34 @@ def fwd_flops(p, k_sel: int) -> float:
 
 
 def kernel_flops(name: str, p, k_sel: int) -> float | None:
-    """Contraction FLOPs one launch of a kernel performs (2*m*n*k per GEMM over selected pairs)."""
+    """Contraction FLOPs one launch of a kernel executes (2*m*n*k per GEMM over selected pairs).
+    The backward recomputes S and dP in both of its passes, so it executes 7 GEMMs per pair
+    where the method needs 5."""
     one_gemm = 2.0 * p.batch * p.heads * p.Nq * (k_sel * p.c) * p.head_dim
     return {"attn_fwd_mfma": 2 * one_gemm,      # S = QK^T, O = PV
             "bwd_dkdv_mfma": 4 * one_gemm,      # S, dP, dV, dK
-            "bwd_dq_mfma": 3 * one_gemm}.get(name)   # S, dP, dQ
+            "bwd_dq_mfma": 3 * one_gemm}.get(name)   # S, dP (both recomputed), dQ
+
+
+def credited_flops(name: str, p, k_sel: int) -> float | None:
+    """The method's FLOPs a kernel is credited with: forward 2 GEMMs; backward 5 GEMMs in all
+    (the FlashAttention count: S recomputed, dP, dV, dK, dQ), of which dK/dV performs 4 and dQ
+    the 1 the other pass has not (its S and dP are repeats)."""
+    one_gemm = 2.0 * p.batch * p.heads * p.Nq * (k_sel * p.c) * p.head_dim
+    return {"attn_fwd_mfma": 2 * one_gemm, "bwd_dkdv_mfma": 4 * one_gemm,
+            "bwd_dq_mfma": 1 * one_gemm}.get(name)
+
+
+def compulsory_bytes(name: str, p, k_sel: int) -> float | None:
+    """Bytes an MFMA kernel must move at least once at a divisible grid with no condition
+    frames: its gathered bf16 operands read once, its outputs written once, its small per-row
+    inputs read once."""
+    tensor = p.batch * p.Nq * p.heads * p.head_dim * 2
+    per_query = p.batch * p.heads * p.Nq * 4
+    idx = p.batch * p.heads * p.nbq * k_sel * 4
+    return {"attn_fwd_mfma": 3 * tensor + tensor + per_query + idx,     # Q, K, V^T; O; LSE; idx
+            "bwd_dkdv_mfma": 4 * tensor + 2 * 2 * tensor + 2 * per_query + idx,  # Q,dO,K,V; dK,dV
+            "bwd_dq_mfma": 4 * tensor + 2 * tensor + 2 * per_query + idx}.get(name)
 
 
 def stage_bytes(name: str, p, k_sel: int) -> float | None:
@@ -58,14 +81,19 @@ def stage_bytes(name: str, p, k_sel: int) -> float | None:
     idx = p.batch * p.heads * p.nbq * k_sel * 4                  # int32 selection
     return {"pool": tensor + means,                             # x in, means out
             "gather_qkv": 3 * 2 * tensor,                       # q, k, v in; ROW/TRANS copies out
-            "gather_qkv_do": 4 * 2 * tensor,                    # q, k, v, dO in; ROW copies out
-            # O, dO in; LSE, Delta (+ pairs) out; CSR transpose: idx in, lists out
-            "bwd_prep": 2 * tensor + 4 * per_query + 2 * idx}.get(name)
+            "bwd_gather_qkv": 3 * 2 * tensor,                   # q, k, v in; ROW copies out
+            "bwd_gather_v": 2 * tensor,                         # v in; ROW copy out
+            # O, dO, LSE in; dO ROW copy and (LSE, Delta) pairs out; CSR transpose: idx in,
+            # lists out
+            "bwd_prep": 3 * tensor + 3 * per_query + 2 * idx}.get(name)
 
 
 def profile_record(stage: str) -> dict:
-    """Counter results of a kernel (profiles/traffic_<stage>.txt: HBM bytes per launch, shader
-    clock), or {} when no measurement exists or the kernel source changed since it was taken."""
+    """Counter results of a kernel (profiles/traffic_<stage>.txt: bytes fetched from beyond L2
+    plus bytes written, per launch, from FETCH_SIZE and WRITE_SIZE scaled by a plain copy; shader
+    clock), or {} when no measurement exists or the kernel source changed since it was taken.
+    FETCH_SIZE counts every byte the L2 fetches, Infinity Cache hits included, so these bytes
+    bound HBM traffic from above."""
     path = os.path.join(ROOT, "profiles", f"traffic_{stage}.txt")
     if not os.path.exists(path):
         return {}
@@ -84,7 +112,7 @@ def profile_record(stage: str) -> dict:
     if h.hexdigest() != kv.get("source_sha256"):
         return {}
     rec = {}
-    for key in ("hbm_bytes_per_launch", "clock_ghz"):
+    for key in ("beyond_l2_bytes_per_launch", "clock_ghz"):
         try:
             rec[key] = float(kv[key])
         except (KeyError, ValueError):
@@ -92,35 +120,134 @@ def profile_record(stage: str) -> dict:
     return rec
 
 
-def cpu_baseline(x, op, idx, r, budget_s: float = 12.0):
-    """The fp64 oracle, as it is, on a bounded sample of the same workload: forward and backward
-    (every GEMM of the algorithm, scatter of key gradients skipped) for query cubes of head 0,
-    taken in order until the time budget is spent."""
+def cpu_baseline(x, op, idx, r, budget_s: float = 20.0):
+    """The fp64 oracle, as it is, on the host cores: the tiny workload (256 tokens) end to end,
+    then a bounded sample of the 720p-class step -- query cubes spread evenly over heads 0, 15 and
+    31, forward then backward (every GEMM of the algorithm for each sampled cube's 145 selected
+    pairs; the key gradients are formed but not scattered).  A first batch of 24 cubes measures
+    the oracle's speed, a second batch is sized to fill the time budget; the rate over both is
+    the baseline, and the full step's time at that rate is reported as extrapolated."""
     import numpy as np
     import oracle as orc
+    from video_dit_block_cube_amd import synth
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         threads = 1
+    # tiny workload in full: pool, select, forward, backward
+    w1 = synth.workload(1)
+    x1 = synth.make_inputs(w1)
+    p1 = orc.Problem(**w1.shape_dict)
+    dO1 = np.random.default_rng(1001).standard_normal(x1["q"].shape).astype(np.float32)
+    t0 = time.perf_counter()
+    qm1, km1 = orc.block_pool(x1["q"], p1), orc.block_pool(x1["k"], p1)
+    idx1, _ = orc.select_topr(qm1, km1, p1, w1.r)
+    orc.sparse_attn_fwd(x1["q"], x1["k"], x1["v"], None, None, idx1, p1, 1 / math.sqrt(p1.head_dim))
+    orc.attn_bwd(x1["q"], x1["k"], x1["v"], dO1, idx1, p1, 1 / math.sqrt(p1.head_dim))
+    tiny_s = time.perf_counter() - t0
+
     scale = 1.0 / math.sqrt(op.head_dim)
     ks = idx.shape[-1]
     per_cube = 4.0 * op.c * (ks * op.c) * op.head_dim * 3.5   # fwd + bwd (2.5x) per query cube
+    heads = [h for h in (0, 15, 31) if h < op.heads]
+    golden = 0.6180339887498949
+
+    def rows_batch(start, n):
+        # cube positions by a golden-ratio sequence: evenly spread over the grid in any prefix
+        out = []
+        for k in range(start, start + n):
+            out.append((0, heads[k % len(heads)], int(((k // len(heads)) * golden % 1.0) * op.nbq)))
+        return out
+
+    def run(rows):
+        orc.attn_fwd_rows(x["q"], x["k"], x["v"], None, None, idx, op, scale, rows)
+        orc.attn_bwd(x["q"], x["k"], x["v"], x["dO"], idx, op, scale, rows=rows, key_cubes=[])
+
     t0 = time.perf_counter()
-    n = 0
-    while True:
-        row = [(0, 0, n)]
-        orc.attn_fwd_rows(x["q"], x["k"], x["v"], None, None, idx, op, scale, row)
-        orc.attn_bwd(x["q"], x["k"], x["v"], x["dO"], idx, op, scale, rows=row, key_cubes=[])
-        n += 1
-        el = time.perf_counter() - t0
-        if (el >= budget_s and n >= 4) or n >= op.nbq:
-            break
-    return {"value": per_cube * n / el / 1e12, "unit": "TFLOP/s", "cores": threads,
-            "kind": "oracle",
-            "sample": f"fp64 oracle fwd+bwd of {n} query cubes (head 0) of the 720p-class workload "
-                      f"in {el:.1f} s; {len(os.sched_getaffinity(0))} host cores visible, "
-                      f"{threads} BLAS threads"}
+    first = rows_batch(0, 24)
+    run(first)
+    t1 = time.perf_counter()
+    per_row = (t1 - t0) / len(first)
+    n2 = max(0, int((budget_s - (t1 - t0)) / max(per_row, 1e-3)))
+    if n2:
+        run(rows_batch(len(first), n2))
+    el = time.perf_counter() - t0
+    n = len(first) + n2
+    rate = per_cube * n / el
+    full_step = 3.5 * 4.0 * op.batch * op.heads * op.Nq * (ks * op.c) * op.head_dim
+    return {"value": rate / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"fp64 oracle fwd+bwd of {n} query cubes of the 720p-class step, spread "
+                      f"evenly over heads {heads} (of {op.batch * op.heads * op.nbq} cubes), in "
+                      f"{el:.1f} s; the 256-token tiny workload end to end in {tiny_s:.3f} s; "
+                      f"{len(os.sched_getaffinity(0))} host cores visible, {threads} BLAS threads",
+            "tiny_workload_s": round(tiny_s, 4),
+            "extrapolated_720p_step_s": round(full_step / rate, 1)}
+
+
+def bench_microbench(bsa, torch, dev, reps=3):
+    """The two limits the attention kernels run against, measured with the library's probe
+    kernels: back-to-back bf16 MFMA on N(0,1) against constant operands at one and two waves per
+    SIMD, and whole 32 KB tile reads at the working sets the kernels see per XCD (a forward key
+    range, half of one, one head's K/V shared by every XCD, the whole 1.5 GB of K/V)."""
+    import numpy as np
+    res = {}
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(31)
+    ops = {"normal": torch.randn(4096, generator=gen, device=dev).to(torch.bfloat16),
+           "constant": torch.full((4096,), 0.5, device=dev, dtype=torch.bfloat16)}
+    n_cu_simd = 1024                          # 256 CUs x 4 SIMDs
+    iters = 40000                             # ~10 ms per launch: long enough for the clock
+    configs = [(name, wps) for wps in (1, 2) for name in ops]
+    sinks = {wps: torch.empty(n_cu_simd * wps * 64, dtype=torch.float32, device=dev)
+             for wps in (1, 2)}
+    for name, wps in configs:                 # warm up every configuration
+        bsa.bsa_probe_mfma(ops[name], n_cu_simd * wps, iters // 10, sinks[wps])
+    torch.cuda.synchronize()
+    times = {c: [] for c in configs}
+    for _ in range(reps):                     # configurations interleaved, so drift hits all alike
+        for name, wps in configs:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            bsa.bsa_probe_mfma(ops[name], n_cu_simd * wps, iters, sinks[wps])
+            e1.record()
+            e1.synchronize()
+            times[(name, wps)].append(e0.elapsed_time(e1))
+    for (name, wps), ms in times.items():
+        flops = n_cu_simd * wps * iters * 8 * 32768.0
+        res[f"mfma_bf16_{name}_{wps}wave_per_simd_tflops"] = round(
+            flops / (float(np.median(ms)) * 1e-3) / 1e12, 1)
+    tile = 32 * 1024
+    buf = torch.empty(1536 * (1 << 20), dtype=torch.uint8, device=dev).view(torch.bfloat16)
+    buf.view(torch.uint8).random_(0, 256, generator=gen)
+    n_tiles = buf.numel() * 2 // tile
+    waves, per_wave = 2048, 64
+    sink = torch.empty(waves * 64, dtype=torch.int32, device=dev)
+    scenarios = {"per_xcd_2.9MB": (int(2.9 * (1 << 20)) // tile, True),
+                 "per_xcd_5.8MB": (int(5.8 * (1 << 20)) // tile, True),
+                 "shared_46MB": (46 * (1 << 20) // tile, False),
+                 "shared_1.5GB": (n_tiles, False)}
+    for name, (span, per_xcd) in scenarios.items():
+        r = torch.randint(0, span, (waves, per_wave), generator=gen, device=dev, dtype=torch.int32)
+        if per_xcd:   # workgroup w runs on XCD w % 8: give each XCD its own span of tiles
+            r += (torch.arange(waves, device=dev, dtype=torch.int32) % 8)[:, None] * span
+        ids = r.contiguous()
+        bsa.bsa_probe_tile_read(buf, tile, ids, per_wave, sink)
+        torch.cuda.synchronize()
+        ms = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            bsa.bsa_probe_tile_read(buf, tile, ids, per_wave, sink)
+            e1.record()
+            e1.synchronize()
+            ms.append(e0.elapsed_time(e1))
+        res[f"tile_read_{name}_TBps"] = round(waves * per_wave * tile /
+                                              (float(np.median(ms)) * 1e-3) / 1e12, 2)
+    del buf
+    res["note"] = ("MFMA: 8 products x iters per wave on 1024 or 2048 one-wave workgroups; tile "
+                   "reads: 2048 waves x 64 random 32 KB tiles, 1 KB wave loads")
+    return res
 
 
 def main() -> int:
@@ -143,6 +270,8 @@ def main() -> int:
                     help="skip the 720p-class step on spatially smooth Q/K")
     ap.add_argument("--no-d64", action="store_true",
                     help="skip the 720p-class forward + backward step at head dim 64")
+    ap.add_argument("--no-microbench", action="store_true",
+                    help="skip the MFMA-rate and tile-read microbenchmarks")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -192,7 +321,8 @@ def main() -> int:
             lambda: bsa.bsa_sparse_attn_fwd(p, t["q"], t["k"], t["v"], idx, ks, scale, o=o,
                                             lse=lse, workspace=ws_f),
             lambda: bsa.bsa_sparse_attn_bwd(p, t["q"], t["k"], t["v"], o, t["dO"], lse, idx, ks,
-                                            scale, dq=dq, dk=dk, dv=dv, workspace=ws_b),
+                                            scale, dq=dq, dk=dk, dv=dv, workspace=ws_b,
+                                            fwd_workspace=ws_f),
         ]
         for ci, c in enumerate(calls):
             if ev is None:
@@ -239,7 +369,10 @@ def main() -> int:
     roofline = {"bound": "mfma", "kernel": dominant, "achieved": round(achieved, 2),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                "traffic": rec.get("hbm_bytes_per_launch"),
+                "traffic": rec.get("beyond_l2_bytes_per_launch"),
+                "traffic_kind": "bytes fetched from beyond L2 (Infinity Cache hits included) + "
+                                "bytes written, per launch (FETCH_SIZE, WRITE_SIZE)",
+                "compulsory_bytes": compulsory_bytes(dominant, p, ks),
                 "flops_per_launch": dom_flops, "avg_launch_ms": round(avg[dominant], 4)}
     if "clock_ghz" in rec:
         # the same MFMA peak at the clock the kernel actually ran at (power-limited)
@@ -249,12 +382,17 @@ def main() -> int:
     per_kernel = {}
     for k, v in avg.items():
         kf = kernel_flops(k, p, ks)
+        kc = credited_flops(k, p, ks)
         kb = stage_bytes(k, p, ks)
         per_kernel[k] = {"avg_ms": round(v, 4),
                          "median_ms": round(float(np.median(stage_ms[k])), 4),
                          "p90_ms": round(float(np.percentile(stage_ms[k], 90)), 4),
-                         **({"tflops": round(kf / (v * 1e-3) / 1e12, 1),
-                             "frac_peak": round(kf / (v * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+                         **({"executed_tflop": round(kf / 1e12, 3),
+                             "credited_tflop": round(kc / 1e12, 3),
+                             "tflops_executed": round(kf / (v * 1e-3) / 1e12, 1),
+                             "tflops_credited": round(kc / (v * 1e-3) / 1e12, 1),
+                             "frac_peak_executed": round(kf / (v * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                                                         4)}
                             if kf else {}),
                          **({"algorithmic_GB": round(kb / 1e9, 3),
                              "achieved_GBps": round(kb / (v * 1e-3) / 1e9, 1),
@@ -276,8 +414,9 @@ def main() -> int:
         "step_ms_median": round(float(np.median(step_ms)), 3),
         "step_ms_p90": round(float(np.percentile(step_ms, 90)), 3),
         "fwd_ms": round(avg.get("gather_qkv", 0) + avg.get("attn_fwd_mfma", 0), 3),
-        "bwd_ms": round(sum(avg.get(k, 0) for k in ("bwd_prep", "gather_qkv_do",
-                                                      "bwd_dkdv_mfma", "bwd_dq_mfma")), 3),
+        "bwd_ms": round(sum(avg.get(k, 0) for k in ("bwd_prep", "bwd_gather_qkv",
+                                                      "bwd_gather_v", "bwd_dkdv_mfma",
+                                                      "bwd_dq_mfma")), 3),
         "kernels": per_kernel,
         "roofline": roofline,
     }
@@ -298,6 +437,10 @@ def main() -> int:
         out["qk_prologue"] = bench_prologue(bsa, torch, dev, p)
     if not args.no_ragged:
         out["real_latent_720p"] = bench_ragged(bsa, synth, torch, dev, args)
+
+    if not args.no_microbench:
+        log("microbenchmarks: MFMA rate, random tile reads")
+        out["microbench"] = bench_microbench(bsa, torch, dev)
 
     if args.calib_copy_mib:
         n = args.calib_copy_mib * (1 << 20) // 4
@@ -360,7 +503,8 @@ def bench_continuation(bsa, synth, orc, torch, dev, args):
     wsb = torch.empty(bsa.bsa_workspace_bytes(p, torch.bfloat16, ks, True), dtype=torch.uint8,
                       device=dev)
     grads = bsa.bsa_sparse_attn_bwd(p, t["q"], t["k"], t["v"], o, d_o, lse, idx, ks, scale,
-                                    workspace=wsb, k_cache=t["k_cache"], v_cache=t["v_cache"])
+                                    workspace=wsb, k_cache=t["k_cache"], v_cache=t["v_cache"],
+                                    fwd_workspace=ws)
     torch.cuda.synchronize()
     evb = [bsa.StageEvents(8) for _ in range(3)]
     for ev in evb:
@@ -368,7 +512,7 @@ def bench_continuation(bsa, synth, orc, torch, dev, args):
             bsa.bsa_sparse_attn_bwd(p, t["q"], t["k"], t["v"], o, d_o, lse, idx, ks, scale,
                                     dq=grads[0], dk=grads[1], dv=grads[2], workspace=wsb,
                                     k_cache=t["k_cache"], v_cache=t["v_cache"],
-                                    dk_cache=grads[3], dv_cache=grads[4])
+                                    dk_cache=grads[3], dv_cache=grads[4], fwd_workspace=ws)
     torch.cuda.synchronize()
     sb: dict[str, list] = {}
     for ev in evb:
@@ -443,7 +587,8 @@ def bench_step(bsa, synth, torch, dev, number, label, reps=5, **over):
                  lambda: bsa.bsa_sparse_attn_fwd(p, t["q"], t["k"], t["v"], idx, ks, scale, o=o,
                                                  lse=lse, workspace=ws_f),
                  lambda: bsa.bsa_sparse_attn_bwd(p, t["q"], t["k"], t["v"], o, t["dO"], lse, idx,
-                                                 ks, scale, dq=dq, dk=dk, dv=dv, workspace=ws_b)]
+                                                 ks, scale, dq=dq, dk=dk, dv=dv, workspace=ws_b,
+                                                 fwd_workspace=ws_f)]
         for e, c in zip(ev, calls):
             with e:
                 c()
@@ -464,8 +609,8 @@ def bench_step(bsa, synth, torch, dev, number, label, reps=5, **over):
             stage.setdefault(name, []).append(ms)
     med = {k: float(np.median(v)) for k, v in stage.items()}
     fwd_ms = med.get("gather_qkv", 0.0) + med.get("attn_fwd_mfma", 0.0)
-    bwd_ms = sum(med.get(k, 0.0) for k in ("bwd_prep", "gather_qkv_do", "bwd_dkdv_mfma",
-                                            "bwd_dq_mfma"))
+    bwd_ms = sum(med.get(k, 0.0) for k in ("bwd_prep", "bwd_gather_qkv", "bwd_gather_v",
+                                            "bwd_dkdv_mfma", "bwd_dq_mfma"))
     step_ms = sum(med.values())
     f = fwd_flops(p, ks)
     return {"workload": f"{label} BSA fwd+bwd: B={w.batch}, Hh={w.heads}, D={w.head_dim}, grid "
@@ -512,7 +657,8 @@ def bench_ragged(bsa, synth, torch, dev, args, reps=3):
             lambda: bsa.bsa_sparse_attn_fwd(p, t["q"], t["k"], t["v"], idx, ks, scale, o=o,
                                             lse=lse, workspace=wsf),
             lambda: bsa.bsa_sparse_attn_bwd(p, t["q"], t["k"], t["v"], o, t["dO"], lse, idx, ks,
-                                            scale, dq=dq, dk=dk, dv=dv, workspace=wsb),
+                                            scale, dq=dq, dk=dk, dv=dv, workspace=wsb,
+                                            fwd_workspace=wsf),
         ]
         for ci, c in enumerate(calls):
             if ev is None:
@@ -589,7 +735,8 @@ def bench_smooth(bsa, synth, torch, dev, reps=3):
                  lambda: bsa.bsa_sparse_attn_fwd(p, t["q"], t["k"], t["v"], idx, ks, scale, o=o,
                                                  lse=lse, workspace=wsf),
                  lambda: bsa.bsa_sparse_attn_bwd(p, t["q"], t["k"], t["v"], o, t["dO"], lse, idx,
-                                                 ks, scale, dq=dq, dk=dk, dv=dv, workspace=wsb)]
+                                                 ks, scale, dq=dq, dk=dk, dv=dv, workspace=wsb,
+                                                 fwd_workspace=wsf)]
         for e, c in zip(ev, calls):
             with e:
                 c()

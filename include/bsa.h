@@ -37,8 +37,9 @@
  *    argument returns an error code and launches nothing.  A launch failure returns BSA_ERR_HIP.
  *    Faults inside kernels surface, as usual for HIP, at the caller's next synchronisation.
  *    No C++ exception crosses this interface.
- *  Threads.  The library keeps no per-call state; concurrent calls on different streams are safe
- *    as long as their output and workspace buffers do not overlap.
+ *  Threads.  The library keeps no state between calls other than per-thread settings
+ *    (bsa_set_kernel_path, bsa_set_tuning, stage events); concurrent calls on different streams
+ *    are safe as long as their output and workspace buffers do not overlap.
  */
 #ifndef BSA_H_
 #define BSA_H_
@@ -161,18 +162,24 @@ bsa_status_t bsa_sparse_attn_fwd(const bsa_problem_t* p, bsa_dtype_t dtype, cons
  *   lse                device, [B, Hh, Nq] fp32
  *   dq, dk, dv         device, [B, Nq, Hh, D] fp32, overwritten
  *   dk_cache, dv_cache device, [B, Nc, Hh, D] fp32, overwritten; NULL iff cond_T == 0
+ *   fwd_ws, fwd_ws_bytes  NULL / 0, or the workspace of the bsa_sparse_attn_fwd call that produced
+ *                      o and lse, unchanged since, with q, k, k_cache unchanged too: the bf16 MFMA
+ *                      path then reads the gathered Q and K it holds instead of gathering them
+ *                      again (read only; ignored by the portable path).  WORKSPACE if it is
+ *                      smaller than that forward's workspace could be.
  *   ws, ws_bytes       device workspace of at least bsa_workspace_bytes(p, dtype, k_sel, 1)
  * With cond_T > 0 only the bf16 MFMA path (64-token cubes) is implemented: UNSUPPORTED otherwise.
  * Precision (bf16): P and dS enter their products rounded to bf16, with fp32 accumulation; at
  * head_dim 128 the dS of dK/dV is formed from the bf16-rounded P.  Results are deterministic
- * (no atomics).
+ * (no atomics), and the same with or without fwd_ws.
  * Errors: INVALID_ARG, SHAPE, UNSUPPORTED, WORKSPACE, HIP. */
 bsa_status_t bsa_sparse_attn_bwd(const bsa_problem_t* p, bsa_dtype_t dtype, const void* q,
                                  const void* k, const void* v, const void* k_cache,
                                  const void* v_cache, const void* o, const void* d_o,
                                  const float* lse, const int32_t* idx, int32_t k_sel,
                                  float softmax_scale, float* dq, float* dk, float* dv,
-                                 float* dk_cache, float* dv_cache, void* ws, size_t ws_bytes,
+                                 float* dk_cache, float* dv_cache, const void* fwd_ws,
+                                 size_t fwd_ws_bytes, void* ws, size_t ws_bytes,
                                  hipStream_t stream);
 
 /* ---- helpers (host only, no HIP calls) ---- */
@@ -202,6 +209,57 @@ const char* bsa_stage_name(int32_t s); /* "" when s is out of range */
  * kernels for 64-token cubes, portable fp32-arithmetic kernels otherwise), 1 = always the
  * portable kernels.  Returns BSA_ERR_INVALID_ARG for other values. */
 bsa_status_t bsa_set_kernel_path(int32_t path);
+
+/* Tuning switches (testing and diagnostics), per host thread, read by every later call on that
+ * thread (bsa_workspace_bytes included, so size the workspace on the thread that calls).  The
+ * defaults are the measured fastest schedules.
+ *   BSA_TUNE_FWD_SPLITS   -1 (default): the size rule; 1: single pass; 2..64: the bf16 MFMA
+ *                         forward splits the key cubes into that many ranges, each attended
+ *                         separately and merged (one XCD's L2 per range).  Changes the
+ *                         summation order, so outputs change at rounding level, and the
+ *                         forward workspace size.
+ *   BSA_TUNE_DKDV_ORDER   1 (default): dK/dV items longest list first; 0: fixed order.  Same bits.
+ *   BSA_TUNE_DQ_PIPELINE  1 (default): software-pipelined dQ where it exists; 0: plain loop.
+ *                         Same bits.
+ * Returns BSA_ERR_INVALID_ARG (setting unchanged) for an unknown key or an out-of-range value. */
+typedef enum {
+  BSA_TUNE_FWD_SPLITS = 0,
+  BSA_TUNE_DKDV_ORDER = 1,
+  BSA_TUNE_DQ_PIPELINE = 2
+} bsa_tune_t;
+bsa_status_t bsa_set_tuning(bsa_tune_t key, int32_t value);
+int32_t bsa_get_tuning(bsa_tune_t key); /* INT32_MIN for an unknown key */
+
+/* Check a selection against the contract of bsa_sparse_attn_fwd / _bwd (every entry in
+ * [0, nbk), every row strictly ascending), asynchronously on `stream`: *bad_rows (device int32,
+ * overwritten) receives the number of rows that break it, readable after the stream
+ * synchronises.  The attention calls themselves do not check (a malformed row gives wrong
+ * gradients, not an error); this is the debugging aid.  Rows of bsa_select_topr always pass.
+ * Errors: INVALID_ARG (null pointer, k_sel), SHAPE, UNSUPPORTED, HIP. */
+bsa_status_t bsa_validate_idx(const bsa_problem_t* p, const int32_t* idx, int32_t k_sel,
+                              int32_t* bad_rows, hipStream_t stream);
+
+/* ---- diagnostics: microbenchmarks of the limits the attention kernels run against ---- */
+
+/* Back-to-back bf16 MFMA (v_mfma_f32_32x32x16_bf16, four independent accumulator chains per
+ * wave) on `waves` one-wave workgroups, iters x 8 products each (32768 FLOP per product), with
+ * the 8 operand fragments of every wave read from `operands` (at least 8192 bytes of bf16).  The
+ * rate bf16 MFMA work reaches on that data: with N(0,1) operands the chip runs at a lower clock
+ * than with constant ones.  sink: device, >= 64 floats per wave, overwritten.
+ * Errors: INVALID_ARG, HIP. */
+bsa_status_t bsa_probe_mfma(const void* operands, size_t operand_bytes, int32_t waves,
+                            int32_t iters, float* sink, size_t sink_bytes, hipStream_t stream);
+
+/* Whole-tile reads: wave w (workgroup w, which runs on XCD w % 8) reads tiles
+ * ids[w * tiles_per_wave + t] of `buf` (tile_bytes each, a multiple of 8192 up to 1 MiB) as
+ * 1 KB wave-wide 16-byte-per-lane loads -- the attention kernels' tile access pattern.  Ids
+ * outside buf are skipped.  buf: device, at most 2^31 - 1 bytes; ids: device, n_ids >= waves *
+ * tiles_per_wave entries; sink: device, >= 64 words per wave, overwritten.
+ * Errors: INVALID_ARG, HIP. */
+bsa_status_t bsa_probe_tile_read(const void* buf, size_t buf_bytes, int32_t tile_bytes,
+                                 const int32_t* ids, size_t n_ids, int32_t waves,
+                                 int32_t tiles_per_wave, uint32_t* sink, size_t sink_bytes,
+                                 hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -103,3 +103,45 @@ def sample_rows(p, heads, per_head, seed=0):
 
 def scale_of(p) -> float:
     return 1.0 / math.sqrt(p.head_dim)
+
+
+def torch_fwd_all_rows(op, t, idx_d, scale, chunk_pairs=600_000):
+    """Every output row of the sparse forward recomputed on the device with plain torch fp32 ops
+    (gather the tokens of each query cube's selected key cubes, softmax, weighted sum), for a
+    grid whose sides are cube multiples.  A full-size cross-check of every row of the kernels,
+    beside the fp64 oracle on sampled rows; the products run in fp32 on contiguous operands.
+    Returns (O [B, Nq, Hh, D] fp32, LSE [B, Hh, Nq] fp32)."""
+    import torch
+    dev = t["q"].device
+    B, Hh, D = op.batch, op.heads, op.head_dim
+    qtok = torch.from_numpy(np.asarray(orc.noise_cube_tokens(op), dtype=np.int64)).to(dev)
+    ktok = qtok
+    out_o = torch.empty((B, op.Nq, Hh, D), dtype=torch.float32, device=dev)
+    out_l = torch.empty((B, Hh, op.Nq), dtype=torch.float32, device=dev)
+    ks = idx_d.shape[-1]
+    n_chunk = max(1, chunk_pairs // (ks * 64))
+    for b in range(B):
+        for h in range(Hh):
+            kn = t["k"][b, :, h].float()[ktok]                       # [nbq, c, D]
+            vn = t["v"][b, :, h].float()[ktok]
+            if op.nbc:
+                ctok = torch.from_numpy(np.asarray(orc.cond_cube_tokens(op),
+                                                   dtype=np.int64)).to(dev)
+                kall = torch.cat([t["k_cache"][b, :, h].float()[ctok], kn])
+                vall = torch.cat([t["v_cache"][b, :, h].float()[ctok], vn])
+            else:
+                kall, vall = kn, vn
+            qall = t["q"][b, :, h].float()[qtok]                     # [nbq, c, D]
+            sel_all = idx_d[b, h].long()
+            for i0 in range(0, op.nbq, n_chunk):
+                i1 = min(op.nbq, i0 + n_chunk)
+                sel = sel_all[i0:i1]
+                ksel = kall[sel].reshape(i1 - i0, ks * op.c, D)
+                vsel = vall[sel].reshape(i1 - i0, ks * op.c, D).contiguous()
+                s = torch.bmm(qall[i0:i1].contiguous(), ksel.transpose(1, 2).contiguous()) * scale
+                lse = torch.logsumexp(s, dim=-1)
+                o = torch.bmm(torch.exp(s - lse[..., None]), vsel)
+                rows = qtok[i0:i1].reshape(-1)
+                out_o[b, rows, h] = o.reshape(-1, D)
+                out_l[b, h, rows] = lse.reshape(-1)
+    return out_o, out_l

@@ -55,11 +55,8 @@ def test_num_selected_and_workspace(L):
     gathers = 3 * 32 * 1440 * 64 * 128 * 2                           # Q, K rows + V^T, bf16
     fwd = bsa.bsa_workspace_bytes(big, torch.bfloat16, 145, False)
     assert fwd > gathers                                             # + key-range partials
-    os.environ["BSA_FWD_SPLITS"] = "1"
-    try:
+    with bsa.tuning(fwd_splits=1):
         assert bsa.bsa_workspace_bytes(big, torch.bfloat16, 145, False) == gathers
-    finally:
-        del os.environ["BSA_FWD_SPLITS"]
     assert bsa.bsa_workspace_bytes(big, torch.float32, 145, False) == 0
     assert bsa.bsa_workspace_bytes(big, torch.bfloat16, 145, True) > gathers
     with pytest.raises(bsa.BsaError):
@@ -106,22 +103,26 @@ def test_argument_errors(L):
     bwd = L.bsa_sparse_attn_bwd
     sc = ctypes.c_float(0.1)
     # argument order: q, k, v, k_cache, v_cache, o, d_o, lse, idx, k_sel, scale,
-    #                 dq, dk, dv, dk_cache, dv_cache, ws, ws_bytes, stream
+    #                 dq, dk, dv, dk_cache, dv_cache, fwd_ws, fwd_ws_bytes, ws,
+    #                 ws_bytes, stream
     cache4 = [FAKE, FAKE]
     # condition frames need all four cache tensors; without them none may be given
     assert bwd(pc, 1, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, FAKE, FAKE, 5, sc,
-               FAKE, FAKE, FAKE, None, None, FAKE, 1 << 40, None) == INVALID
+               FAKE, FAKE, FAKE, None, None, None, 0, FAKE, 1 << 40, None) == INVALID
     assert bwd(pc, 1, FAKE, FAKE, FAKE, *cache4, FAKE, FAKE, FAKE, FAKE, 5, sc,
-               FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 40, None) == INVALID
+               FAKE, FAKE, FAKE, FAKE, None, None, 0, FAKE, 1 << 40, None) == INVALID
     assert bwd(p, 1, FAKE, FAKE, FAKE, *cache4, FAKE, FAKE, FAKE, FAKE, 3, sc,
-               FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, None) == INVALID
+               FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, FAKE, 1 << 40, None) == INVALID
     # cache gradients exist on the bf16 MFMA path only
     assert bwd(pc, 0, FAKE, FAKE, FAKE, *cache4, FAKE, FAKE, FAKE, FAKE, 5, sc,
-               FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, None) == UNSUPPORTED
+               FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, FAKE, 1 << 40, None) == UNSUPPORTED
     assert bwd(p, 1, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, FAKE, FAKE, 3, sc,
-               FAKE, FAKE, FAKE, None, None, FAKE, 8, None) == WORKSPACE
+               FAKE, FAKE, FAKE, None, None, None, 0, FAKE, 8, None) == WORKSPACE
     assert bwd(p, 1, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, FAKE, None, 3, sc,
-               FAKE, FAKE, FAKE, None, None, FAKE, 1 << 40, None) == INVALID
+               FAKE, FAKE, FAKE, None, None, None, 0, FAKE, 1 << 40, None) == INVALID
+    # a forward workspace smaller than the forward's gathered operands is refused
+    assert bwd(p, 1, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, FAKE, FAKE, 3, sc,
+               FAKE, FAKE, FAKE, None, None, FAKE, 64, FAKE, 1 << 40, None) == WORKSPACE
     # the condition-mode workspace covers K/V gathers over every key cube
     big = bsa.Problem(1, 32, 128, 24, 48, 80, 4, 4, 4, cond_T=12)
     plain = bsa.Problem(1, 32, 128, 12, 48, 80, 4, 4, 4)
@@ -174,6 +175,41 @@ def test_size_limits(L):
     ks = L.bsa_num_selected(pc, 1)
     assert ks == 39808 + 1 + 1
     assert L.bsa_sparse_attn_bwd(pc, 1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ks,
-                                 sc, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40,
+                                 sc, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, FAKE, 1 << 40,
                                  None) == UNSUPPORTED
     assert b"39936" in L.bsa_last_error()
+
+
+def test_tuning_switches_are_checked_and_per_thread(L):
+    import threading
+    import torch
+    big = bsa.Problem(1, 32, 128, 24, 48, 80, 4, 4, 4)
+    assert bsa.bsa_get_tuning(bsa.BSA_TUNE_FWD_SPLITS) == -1
+    assert bsa.bsa_get_tuning(bsa.BSA_TUNE_DKDV_ORDER) == 1
+    assert bsa.bsa_get_tuning(bsa.BSA_TUNE_DQ_PIPELINE) == 1
+    assert L.bsa_get_tuning(7) == -(2 ** 31)
+    for key, bad in ((bsa.BSA_TUNE_FWD_SPLITS, 0), (bsa.BSA_TUNE_FWD_SPLITS, 65),
+                     (bsa.BSA_TUNE_FWD_SPLITS, -2), (bsa.BSA_TUNE_DKDV_ORDER, 2),
+                     (bsa.BSA_TUNE_DQ_PIPELINE, -1), (9, 1)):
+        assert L.bsa_set_tuning(key, bad) == INVALID
+    assert bsa.bsa_get_tuning(bsa.BSA_TUNE_FWD_SPLITS) == -1      # a rejected value changes nothing
+    auto = bsa.bsa_workspace_bytes(big, torch.bfloat16, 145, False)
+    with bsa.tuning(fwd_splits=16):
+        assert bsa.bsa_get_tuning(bsa.BSA_TUNE_FWD_SPLITS) == 16
+        assert bsa.bsa_workspace_bytes(big, torch.bfloat16, 145, False) > auto
+        seen = []
+        t = threading.Thread(target=lambda: seen.append(bsa.bsa_get_tuning(bsa.BSA_TUNE_FWD_SPLITS)))
+        t.start()
+        t.join()
+        assert seen == [-1]                                          # other threads keep their own
+    assert bsa.bsa_workspace_bytes(big, torch.bfloat16, 145, False) == auto
+
+
+def test_validate_idx_rejects_bad_arguments_on_host(L):
+    p = _p()
+    bad = ctypes.c_void_p(0x10000)
+    assert L.bsa_validate_idx(ctypes.byref(p), None, 3, bad, None) == INVALID
+    assert L.bsa_validate_idx(ctypes.byref(p), FAKE, 3, None, None) == INVALID
+    assert L.bsa_validate_idx(ctypes.byref(p), FAKE, 0, bad, None) == INVALID   # k_sel < 1
+    assert L.bsa_validate_idx(ctypes.byref(p), FAKE, 9, bad, None) == INVALID   # k_sel > nbk
+    assert L.bsa_validate_idx(ctypes.byref(_p(head_dim=96)), FAKE, 1, bad, None) == UNSUPPORTED

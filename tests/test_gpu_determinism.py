@@ -11,14 +11,20 @@ from video_dit_block_cube_amd import bsa, synth
 pytestmark = pytest.mark.gpu
 
 
-def _run(p, t, r, ks, scale):
+def _run(p, t, r, ks, scale, reuse_fwd_ws=False):
+    import torch
     qm = bsa.bsa_block_pool(p, t["q"])
     km = bsa.bsa_block_pool(p, t["k"])
     idx, mask = bsa.bsa_select_topr(p, qm, km, r)
+    dt = t["q"].dtype
+    ws_f = torch.empty(bsa.bsa_workspace_bytes(p, dt, ks, False), dtype=torch.uint8,
+                       device=t["q"].device)
     o, lse = bsa.bsa_sparse_attn_fwd(p, t["q"], t["k"], t["v"], idx, ks, scale,
-                                     t.get("k_cache"), t.get("v_cache"))
+                                     t.get("k_cache"), t.get("v_cache"),
+                                     workspace=ws_f if ws_f.numel() else None)
     grads = bsa.bsa_sparse_attn_bwd(p, t["q"], t["k"], t["v"], o, t["dO"], lse, idx, ks, scale,
-                                    k_cache=t.get("k_cache"), v_cache=t.get("v_cache"))
+                                    k_cache=t.get("k_cache"), v_cache=t.get("v_cache"),
+                                    fwd_workspace=ws_f if reuse_fwd_ws else None)
     if not isinstance(grads, tuple):
         grads = (grads,)
     import torch
@@ -30,12 +36,10 @@ def _run(p, t, r, ks, scale):
 @pytest.mark.parametrize("number, over, splits", [
     (5, (("heads", 4),), None),                                  # 480p grid, default 8-range split
     (4, (("heads", 2), ("T", 12), ("H", 24), ("W", 40), ("cond_T", 4)), None),  # continuation
-    (5, (("heads", 2), ("H", 30), ("W", 50)), "16"),             # ragged grid, 16 ranges
+    (5, (("heads", 2), ("H", 30), ("W", 50)), 16),             # ragged grid, 16 ranges
     (5, (("heads", 4), ("head_dim", 64)), None),                 # D = 64: 16-query dK/dV steps
 ])
-def test_bit_identical_reruns(number, over, splits, monkeypatch):
-    if splits is not None:
-        monkeypatch.setenv("BSA_FWD_SPLITS", splits)
+def test_bit_identical_reruns(number, over, splits):
     w = synth.workload(number, **dict(over))
     print_case(f"determinism {w.name} {dict(over)} splits={splits}")
     x = synth.make_inputs(w)
@@ -45,8 +49,9 @@ def test_bit_identical_reruns(number, over, splits, monkeypatch):
     p, op = bsa.Problem(**w.shape_dict), orc.Problem(**w.shape_dict)
     t = {k: to_dev(v, w.dtype) for k, v in x.items()}
     ks, scale = orc.num_selected(op, w.r), scale_of(op)
-    first = _run(p, t, w.r, ks, scale)
-    second = _run(p, t, w.r, ks, scale)
+    with bsa.tuning(fwd_splits=-1 if splits is None else splits):
+        first = _run(p, t, w.r, ks, scale)
+        second = _run(p, t, w.r, ks, scale)
     names = ["q_mean", "k_mean", "idx", "mask", "O", "LSE", "dQ", "dK", "dV", "dK_cache",
              "dV_cache"]
     for name, a, b in zip(names, first, second):
@@ -59,8 +64,8 @@ def test_bit_identical_reruns(number, over, splits, monkeypatch):
     (4, (("heads", 2), ("T", 12), ("H", 24), ("W", 40), ("cond_T", 4))),  # condition cubes
     (5, (("heads", 2), ("head_dim", 64))),                              # D = 64: one-wave dK/dV
 ])
-def test_dkdv_dispatch_order_changes_nothing(number, over, monkeypatch):
-    """dK/dV items run longest-first by default; the fixed id order (BSA_DKDV_ORDER=0) must give
+def test_dkdv_dispatch_order_changes_nothing(number, over):
+    """dK/dV items run longest-first by default; the fixed id order (BSA_TUNE_DKDV_ORDER 0) must give
     the same bits, since no item's arithmetic depends on when it runs."""
     w = synth.workload(number, **dict(over))
     print_case(f"dK/dV dispatch order {w.name} {dict(over)}")
@@ -72,8 +77,8 @@ def test_dkdv_dispatch_order_changes_nothing(number, over, monkeypatch):
     t = {k: to_dev(v, w.dtype) for k, v in x.items()}
     ks, scale = orc.num_selected(op, w.r), scale_of(op)
     longest_first = _run(p, t, w.r, ks, scale)
-    monkeypatch.setenv("BSA_DKDV_ORDER", "0")
-    fixed = _run(p, t, w.r, ks, scale)
+    with bsa.tuning(dkdv_order=0):
+        fixed = _run(p, t, w.r, ks, scale)
     names = ["q_mean", "k_mean", "idx", "mask", "O", "LSE", "dQ", "dK", "dV", "dK_cache",
              "dV_cache"]
     for name, a, b in zip(names, longest_first, fixed):
@@ -84,9 +89,9 @@ def test_dkdv_dispatch_order_changes_nothing(number, over, monkeypatch):
     (5, (("heads", 4),)),                                               # D = 128: pipelined dQ
     (4, (("heads", 2), ("T", 12), ("H", 24), ("W", 40), ("cond_T", 4))),  # condition cubes
 ])
-def test_dq_pipeline_changes_nothing(number, over, monkeypatch):
+def test_dq_pipeline_changes_nothing(number, over):
     """At head_dim 128 on grids without partial cubes dQ runs a software-pipelined loop; the plain
-    loop (BSA_DQ_PIPELINE=0) must give the same bits, since each tile's arithmetic and the order
+    loop (BSA_TUNE_DQ_PIPELINE 0) must give the same bits, since each tile's arithmetic and the order
     of the dQ updates are the same."""
     w = synth.workload(number, **dict(over))
     print_case(f"dQ pipeline {w.name} {dict(over)}")
@@ -98,9 +103,35 @@ def test_dq_pipeline_changes_nothing(number, over, monkeypatch):
     t = {k: to_dev(v, w.dtype) for k, v in x.items()}
     ks, scale = orc.num_selected(op, w.r), scale_of(op)
     pipelined = _run(p, t, w.r, ks, scale)
-    monkeypatch.setenv("BSA_DQ_PIPELINE", "0")
-    plain = _run(p, t, w.r, ks, scale)
+    with bsa.tuning(dq_pipeline=0):
+        plain = _run(p, t, w.r, ks, scale)
     names = ["q_mean", "k_mean", "idx", "mask", "O", "LSE", "dQ", "dK", "dV", "dK_cache",
              "dV_cache"]
     for name, a, b in zip(names, pipelined, plain):
         assert a.tobytes() == b.tobytes(), f"{name} differs between the dQ loops"
+
+
+@pytest.mark.parametrize("number, over", [
+    (5, (("heads", 4),)),                                               # D = 128
+    (4, (("heads", 2), ("T", 12), ("H", 24), ("W", 40), ("cond_T", 4))),  # condition cubes
+    (5, (("heads", 2), ("head_dim", 64))),                              # D = 64
+    (5, (("heads", 2), ("H", 30), ("W", 50))),                          # ragged grid
+])
+def test_bwd_reusing_forward_gathers_changes_nothing(number, over):
+    """The backward may read the gathered Q and K rows from the forward's workspace instead of
+    gathering them again: the gradients must be the same bit for bit."""
+    w = synth.workload(number, **dict(over))
+    print_case(f"bwd with the forward's gathers {w.name} {dict(over)}")
+    x = synth.make_inputs(w)
+    if "dO" not in x:
+        x["dO"] = synth.round_to_bf16(
+            np.random.default_rng(80).standard_normal(x["q"].shape).astype(np.float32))
+    p, op = bsa.Problem(**w.shape_dict), orc.Problem(**w.shape_dict)
+    t = {k: to_dev(v, w.dtype) for k, v in x.items()}
+    ks, scale = orc.num_selected(op, w.r), scale_of(op)
+    own = _run(p, t, w.r, ks, scale)
+    reused = _run(p, t, w.r, ks, scale, reuse_fwd_ws=True)
+    names = ["q_mean", "k_mean", "idx", "mask", "O", "LSE", "dQ", "dK", "dV", "dK_cache",
+             "dV_cache"]
+    for name, a, b in zip(names, own, reused):
+        assert a.tobytes() == b.tobytes(), f"{name} differs with the forward's gathers"

@@ -76,9 +76,8 @@ def test_ragged_fwd(number, over, r, path):
                  max_abs=1e-4 if w.dtype == "f32" else 2e-3, rel=1e-5)
 
 
-@pytest.mark.parametrize("splits", ["3", "8"])
-def test_ragged_fwd_key_range_split(splits, monkeypatch):
-    monkeypatch.setenv("BSA_FWD_SPLITS", splits)
+@pytest.mark.parametrize("splits", [3, 8])
+def test_ragged_fwd_key_range_split(splits):
     for number, over, r in ((2, (("batch", 2), ("heads", 2), ("T", 8), ("H", 18), ("W", 22)), 5),
                             (4, (("heads", 2), ("T", 12), ("H", 10), ("W", 14), ("cond_T", 4)), 3)):
         w, x = cached_inputs(number, over)
@@ -87,8 +86,9 @@ def test_ragged_fwd_key_range_split(splits, monkeypatch):
         idx = _oracle_idx(x, op, r)
         t = {k: to_dev(v, w.dtype) for k, v in x.items()}
         ks, scale = orc.num_selected(op, r), scale_of(op)
-        o, lse = bsa.bsa_sparse_attn_fwd(p, t["q"], t["k"], t["v"], _idx_dev(idx), ks, scale,
-                                         t.get("k_cache"), t.get("v_cache"))
+        with bsa.tuning(fwd_splits=splits):
+            o, lse = bsa.bsa_sparse_attn_fwd(p, t["q"], t["k"], t["v"], _idx_dev(idx), ks, scale,
+                                             t.get("k_cache"), t.get("v_cache"))
         O, LSE = orc.sparse_attn_fwd(x["q"], x["k"], x["v"], x.get("k_cache"), x.get("v_cache"),
                                      idx, op, scale)
         assert_close(o.float().cpu().numpy(), O, "bf16", "O")

@@ -103,7 +103,7 @@ def lib() -> ctypes.CDLL:
             "bsa_sparse_attn_fwd": (i32, [P, i32, vp, vp, vp, vp, vp, vp, i32, f32, vp, vp, vp,
                                           sz, vp]),
             "bsa_sparse_attn_bwd": (i32, [P, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, f32,
-                                          vp, vp, vp, vp, vp, vp, sz, vp]),
+                                          vp, vp, vp, vp, vp, vp, sz, vp, sz, vp]),
             "bsa_num_selected": (i32, [P, i32]),
             "bsa_workspace_bytes": (sz, [P, i32, i32, i32]),
             "bsa_status_string": (ctypes.c_char_p, [i32]),
@@ -112,6 +112,11 @@ def lib() -> ctypes.CDLL:
             "bsa_stage_count": (i32, []),
             "bsa_stage_name": (ctypes.c_char_p, [i32]),
             "bsa_set_kernel_path": (i32, [i32]),
+            "bsa_set_tuning": (i32, [i32, i32]),
+            "bsa_get_tuning": (i32, [i32]),
+            "bsa_validate_idx": (i32, [P, vp, i32, vp, vp]),
+            "bsa_probe_mfma": (i32, [vp, sz, i32, i32, vp, sz, vp]),
+            "bsa_probe_tile_read": (i32, [vp, sz, i32, vp, sz, i32, i32, vp, sz, vp]),
         }
         for name, (res, args) in sigs.items():
             fn = getattr(L, name)
@@ -168,6 +173,51 @@ def bsa_status_string(status: int) -> str:
 
 def bsa_set_kernel_path(path: int) -> None:
     _check(lib().bsa_set_kernel_path(int(path)))
+
+
+BSA_TUNE_FWD_SPLITS, BSA_TUNE_DKDV_ORDER, BSA_TUNE_DQ_PIPELINE = 0, 1, 2
+
+
+def bsa_set_tuning(key: int, value: int) -> None:
+    """Per-thread tuning switch (see include/bsa.h): forward key-range count (-1 automatic),
+    longest-first dK/dV order, pipelined dQ."""
+    _check(lib().bsa_set_tuning(int(key), int(value)))
+
+
+def bsa_get_tuning(key: int) -> int:
+    return int(lib().bsa_get_tuning(int(key)))
+
+
+class tuning:
+    """Context manager: set tuning switches on this thread, restore them on exit.
+    Example: `with bsa.tuning(fwd_splits=1): ...`"""
+    _KEYS = {"fwd_splits": BSA_TUNE_FWD_SPLITS, "dkdv_order": BSA_TUNE_DKDV_ORDER,
+             "dq_pipeline": BSA_TUNE_DQ_PIPELINE}
+
+    def __init__(self, **settings):
+        self.settings = {self._KEYS[k]: int(v) for k, v in settings.items()}
+        self.saved = {}
+
+    def __enter__(self):
+        for key, value in self.settings.items():
+            self.saved[key] = bsa_get_tuning(key)
+            bsa_set_tuning(key, value)
+        return self
+
+    def __exit__(self, *exc):
+        for key, value in self.saved.items():
+            bsa_set_tuning(key, value)
+        return False
+
+
+def bsa_validate_idx(p: Problem, idx: torch.Tensor, k_sel: int) -> int:
+    """Number of rows of idx that break the attention calls' contract (an entry outside
+    [0, nbk) or a row not strictly ascending); synchronises the stream to read it."""
+    bad = torch.empty(1, dtype=torch.int32, device=idx.device)
+    _check(lib().bsa_validate_idx(ctypes.byref(p.c_struct()),
+                                  _ptr(idx, "idx", (p.batch, p.heads, p.nbq, k_sel), torch.int32),
+                                  int(k_sel), _ptr(bad, "bad_rows"), _stream(idx)))
+    return int(bad.item())
 
 
 def bsa_block_pool(p: Problem, x: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
@@ -266,9 +316,11 @@ def bsa_sparse_attn_fwd(p: Problem, q, k, v, idx, k_sel: int, softmax_scale: flo
 def bsa_sparse_attn_bwd(p: Problem, q, k, v, o, d_o, lse, idx, k_sel: int,
                         softmax_scale: float | None = None, dq=None, dk=None, dv=None,
                         workspace=None, k_cache=None, v_cache=None, dk_cache=None,
-                        dv_cache=None):
+                        dv_cache=None, fwd_workspace=None):
     """-> (dq, dk, dv) fp32 [B, Nq, Hh, D]; with condition frames (k_cache, v_cache given)
-    -> (dq, dk, dv, dk_cache, dv_cache), the last two [B, Nc, Hh, D]."""
+    -> (dq, dk, dv, dk_cache, dv_cache), the last two [B, Nc, Hh, D].  fwd_workspace: the
+    workspace of the forward call that produced o and lse (inputs unchanged since), whose
+    gathered Q and K the backward then reuses."""
     scale = 1.0 / math.sqrt(p.head_dim) if softmax_scale is None else float(softmax_scale)
     shp = (p.batch, p.Nq, p.heads, p.head_dim)
     shc = (p.batch, p.Nc, p.heads, p.head_dim)
@@ -293,6 +345,8 @@ def bsa_sparse_attn_bwd(p: Problem, q, k, v, o, d_o, lse, idx, k_sel: int,
         _ptr(dk, "dk", shp, torch.float32), _ptr(dv, "dv", shp, torch.float32),
         _ptr(dk_cache if cached else None, "dk_cache", shc, torch.float32),
         _ptr(dv_cache if cached else None, "dv_cache", shc, torch.float32),
+        _ptr(fwd_workspace, "fwd_workspace"),
+        ctypes.c_size_t(0 if fwd_workspace is None else fwd_workspace.numel()),
         _ptr(ws, "workspace"), ctypes.c_size_t(ws.numel()), _stream(q)))
     if cached:
         return dq, dk, dv, dk_cache, dv_cache
@@ -341,3 +395,22 @@ class StageEvents:
             self.hip.hipEventElapsedTime(ctypes.byref(ms), self.arr[s], self.arr[s + 1])
             out.append((name, float(ms.value)))
         return out
+
+
+# ---- diagnostics: microbenchmarks (see include/bsa.h) ----
+def bsa_probe_mfma(operands: torch.Tensor, waves: int, iters: int, sink: torch.Tensor) -> None:
+    """Back-to-back bf16 MFMA on `waves` waves, iters x 8 products each (32768 FLOP each)."""
+    _check(lib().bsa_probe_mfma(_ptr(operands, "operands"), operands.numel() * operands.element_size(),
+                                int(waves), int(iters), _ptr(sink, "sink"),
+                                sink.numel() * sink.element_size(), _stream(operands)))
+
+
+def bsa_probe_tile_read(buf: torch.Tensor, tile_bytes: int, ids: torch.Tensor,
+                        tiles_per_wave: int, sink: torch.Tensor) -> None:
+    """Wave w reads tiles ids[w, :] of buf (tile_bytes each) as 1 KB wave loads."""
+    waves = ids.numel() // int(tiles_per_wave)
+    _check(lib().bsa_probe_tile_read(_ptr(buf, "buf"), buf.numel() * buf.element_size(),
+                                     int(tile_bytes), _ptr(ids, "ids", dtype=torch.int32),
+                                     ids.numel(), int(waves), int(tiles_per_wave),
+                                     _ptr(sink, "sink"), sink.numel() * sink.element_size(),
+                                     _stream(buf)))

@@ -7,9 +7,9 @@
 // paragraph; "LongCat-Video 高效長視頻生成探索世界模型的第壹步", meituan.com talk, section 2.1),
 // and the backward (same talk, section 2.2).  Every check runs on the host before any HIP call.
 #include <cmath>
-#include <cstdlib>
 #include <cstring>
 #include <exception>
+#include <climits>
 #include <string>
 
 #include "bsa.h"
@@ -25,6 +25,12 @@ thread_local int t_nevents = 0;
 thread_local const char* t_stage_names[16];
 thread_local int t_nstages = 0;
 thread_local int t_path = 0;
+// Tuning switches (bsa_set_tuning): forward key-range count (-1 = size rule), longest-first
+// dK/dV dispatch, pipelined dQ.
+thread_local int t_fwd_splits = -1;
+thread_local int t_dkdv_order = 1;
+thread_local int t_dq_pipeline = 1;
+constexpr int kMaxFwdSplits = 64;
 
 constexpr size_t kAlign = 256;
 // Cubes per segment: one selection row (a 4-byte key per noise cube), the query descriptor and a
@@ -141,15 +147,17 @@ BwdWs bwd_layout(const Geom& g, bool mfma, int k_sel) {
   return w;
 }
 
-// Key-range split count of the MFMA forward: BSA_FWD_SPLITS overrides the size-based choice
-// (tuning aid; 1 disables the split).
-int fwd_splits(const Geom& g, int k_sel) {
-  const char* env = std::getenv("BSA_FWD_SPLITS");
-  return fwd_split_ranges(g, k_sel, env ? std::atoi(env) : -1);
-}
+// Key-range split count of the MFMA forward: the size rule, or this thread's
+// BSA_TUNE_FWD_SPLITS setting (1 disables the split).
+int fwd_splits(const Geom& g, int k_sel) { return fwd_split_ranges(g, k_sel, t_fwd_splits); }
 
 // Forward workspace (MFMA path): K rows + V^T over all nbk key cubes, Q rows over the nbq query
-// cubes, the key-range partials, then (ragged grids) the key cubes' slot masks.
+// cubes, the key-range partials, then (ragged grids) the key cubes' slot masks.  The gathered
+// operands sit at fixed offsets whatever the split count: K rows at 0, V^T next, then Q rows.
+size_t fwd_q_rows_offset(const Geom& g) { return 2 * align_up(gather_bytes(g, true)); }
+size_t fwd_ws_bytes_min(const Geom& g, bool mfma) {
+  return mfma ? fwd_q_rows_offset(g) + gather_bytes(noise_only(g), true) : 0;
+}
 size_t fwd_ws(const Geom& g, bool mfma, int k_sel) {
   if (!mfma) return 0;
   return 2 * align_up(gather_bytes(g, true)) + align_up(gather_bytes(noise_only(g), true)) +
@@ -165,6 +173,66 @@ bsa_status_t guarded(F&& f) {
   } catch (...) {
     return fail(BSA_ERR_INTERNAL, "internal error");
   }
+}
+
+bsa_status_t fwd_impl(const bsa_problem_t* p, bsa_dtype_t dtype, const void* q,
+                      const void* k, const void* v, const void* k_cache, const void* v_cache,
+                      const int32_t* idx, int32_t k_sel, float softmax_scale, void* o, float* lse,
+                      void* ws,
+                      size_t ws_bytes, hipStream_t stream, const char* ws_what) {
+  return guarded([&]() -> bsa_status_t {
+    Geom g;
+    bsa_status_t st = check_problem(p, &g);
+    if (st != BSA_OK) return st;
+    if ((st = check_dtype(dtype)) != BSA_OK) return st;
+    if ((st = check_ksel(g, k_sel)) != BSA_OK) return st;
+    if (!q || !k || !v || !idx || !o || !lse)
+      return fail(BSA_ERR_INVALID_ARG, "q, k, v, idx, o and lse must be non-NULL");
+    if (g.condT > 0 && (!k_cache || !v_cache))
+      return fail(BSA_ERR_INVALID_ARG, "cond_T > 0 needs k_cache and v_cache");
+    if (g.condT == 0 && (k_cache || v_cache))
+      return fail(BSA_ERR_INVALID_ARG, "k_cache / v_cache given but cond_T == 0");
+    if (!std::isfinite(softmax_scale)) return fail(BSA_ERR_INVALID_ARG, "softmax_scale not finite");
+    const bool mfma = use_mfma(g, dtype);
+    const size_t need = fwd_ws(g, mfma, k_sel);
+    if (need > 0 && (!ws || ws_bytes < need))
+      return fail(BSA_ERR_WORKSPACE, std::string(ws_what) + " holds " + std::to_string(ws_bytes) +
+                                         " bytes; this problem needs " + std::to_string(need));
+    Stages stages(stream);
+    if (mfma) {
+      char* base = static_cast<char*>(ws);
+      const Geom gq = noise_only(g);
+      bf16_t* krow = reinterpret_cast<bf16_t*>(base);
+      bf16_t* vtr = reinterpret_cast<bf16_t*>(base + align_up(gather_bytes(g, true)));
+      bf16_t* qrow = reinterpret_cast<bf16_t*>(base + 2 * align_up(gather_bytes(g, true)));
+      void* split_ws = base + 2 * align_up(gather_bytes(g, true)) +
+                       align_up(gather_bytes(gq, true));
+      st = hip_status(launch_gather(g, k, k_cache, GATHER_ROW, krow, nullptr, stream),
+                      "gather K");
+      if (st != BSA_OK) return st;
+      st = hip_status(launch_gather(g, v, v_cache, GATHER_TRANS, nullptr, vtr, stream),
+                      "gather V");
+      if (st != BSA_OK) return st;
+      st = hip_status(launch_gather(gq, q, nullptr, GATHER_ROW, qrow, nullptr, stream),
+                      "gather Q");
+      if (st != BSA_OK) return st;
+      stages.done("gather_qkv");
+      const int ns = fwd_splits(g, k_sel);
+      uint2* kmask = g.ragged ? reinterpret_cast<uint2*>(static_cast<char*>(split_ws) +
+                                                         align_up(fwd_split_bytes(g, ns)))
+                              : nullptr;
+      st = hip_status(launch_fwd_mfma(g, qrow, krow, vtr, idx, k_sel, softmax_scale, o, lse, ns,
+                                      split_ws, kmask, stream),
+                      "attention forward launch");
+      stages.done("attn_fwd_mfma");
+    } else {
+      st = hip_status(launch_fwd_simt(g, dtype == BSA_BF16, q, k, v, k_cache, v_cache, idx,
+                                      k_sel, softmax_scale, o, lse, stream),
+                      "attention forward launch");
+      stages.done("attn_fwd_simt");
+    }
+    return st;
+  });
 }
 
 }  // namespace
@@ -241,58 +309,8 @@ bsa_status_t bsa_sparse_attn_fwd(const bsa_problem_t* p, bsa_dtype_t dtype, cons
                                  const void* v_cache, const int32_t* idx, int32_t k_sel,
                                  float softmax_scale, void* o, float* lse, void* ws,
                                  size_t ws_bytes, hipStream_t stream) {
-  return guarded([&]() -> bsa_status_t {
-    Geom g;
-    bsa_status_t st = check_problem(p, &g);
-    if (st != BSA_OK) return st;
-    if ((st = check_dtype(dtype)) != BSA_OK) return st;
-    if ((st = check_ksel(g, k_sel)) != BSA_OK) return st;
-    if (!q || !k || !v || !idx || !o || !lse)
-      return fail(BSA_ERR_INVALID_ARG, "q, k, v, idx, o and lse must be non-NULL");
-    if (g.condT > 0 && (!k_cache || !v_cache))
-      return fail(BSA_ERR_INVALID_ARG, "cond_T > 0 needs k_cache and v_cache");
-    if (g.condT == 0 && (k_cache || v_cache))
-      return fail(BSA_ERR_INVALID_ARG, "k_cache / v_cache given but cond_T == 0");
-    if (!std::isfinite(softmax_scale)) return fail(BSA_ERR_INVALID_ARG, "softmax_scale not finite");
-    const bool mfma = use_mfma(g, dtype);
-    const size_t need = fwd_ws(g, mfma, k_sel);
-    if (need > 0 && (!ws || ws_bytes < need))
-      return fail(BSA_ERR_WORKSPACE, "workspace smaller than bsa_workspace_bytes()");
-    Stages stages(stream);
-    if (mfma) {
-      char* base = static_cast<char*>(ws);
-      const Geom gq = noise_only(g);
-      bf16_t* krow = reinterpret_cast<bf16_t*>(base);
-      bf16_t* vtr = reinterpret_cast<bf16_t*>(base + align_up(gather_bytes(g, true)));
-      bf16_t* qrow = reinterpret_cast<bf16_t*>(base + 2 * align_up(gather_bytes(g, true)));
-      void* split_ws = base + 2 * align_up(gather_bytes(g, true)) +
-                       align_up(gather_bytes(gq, true));
-      st = hip_status(launch_gather(g, k, k_cache, GATHER_ROW, krow, nullptr, stream),
-                      "gather K");
-      if (st != BSA_OK) return st;
-      st = hip_status(launch_gather(g, v, v_cache, GATHER_TRANS, nullptr, vtr, stream),
-                      "gather V");
-      if (st != BSA_OK) return st;
-      st = hip_status(launch_gather(gq, q, nullptr, GATHER_ROW, qrow, nullptr, stream),
-                      "gather Q");
-      if (st != BSA_OK) return st;
-      stages.done("gather_qkv");
-      const int ns = fwd_splits(g, k_sel);
-      uint2* kmask = g.ragged ? reinterpret_cast<uint2*>(static_cast<char*>(split_ws) +
-                                                         align_up(fwd_split_bytes(g, ns)))
-                              : nullptr;
-      st = hip_status(launch_fwd_mfma(g, qrow, krow, vtr, idx, k_sel, softmax_scale, o, lse, ns,
-                                      split_ws, kmask, stream),
-                      "attention forward launch");
-      stages.done("attn_fwd_mfma");
-    } else {
-      st = hip_status(launch_fwd_simt(g, dtype == BSA_BF16, q, k, v, k_cache, v_cache, idx,
-                                      k_sel, softmax_scale, o, lse, stream),
-                      "attention forward launch");
-      stages.done("attn_fwd_simt");
-    }
-    return st;
-  });
+  return fwd_impl(p, dtype, q, k, v, k_cache, v_cache, idx, k_sel, softmax_scale, o, lse, ws,
+                  ws_bytes, stream, "workspace");
 }
 
 bsa_status_t bsa_sparse_attn_bwd(const bsa_problem_t* p, bsa_dtype_t dtype, const void* q,
@@ -300,7 +318,8 @@ bsa_status_t bsa_sparse_attn_bwd(const bsa_problem_t* p, bsa_dtype_t dtype, cons
                                  const void* v_cache, const void* o, const void* d_o,
                                  const float* lse, const int32_t* idx, int32_t k_sel,
                                  float softmax_scale, float* dq, float* dk, float* dv,
-                                 float* dk_cache, float* dv_cache, void* ws, size_t ws_bytes,
+                                 float* dk_cache, float* dv_cache, const void* fwd_ws,
+                                 size_t fwd_ws_bytes, void* ws, size_t ws_bytes,
                                  hipStream_t stream) {
   return guarded([&]() -> bsa_status_t {
     Geom g;
@@ -326,6 +345,11 @@ bsa_status_t bsa_sparse_attn_bwd(const bsa_problem_t* p, bsa_dtype_t dtype, cons
     const BwdWs w = bwd_layout(g, mfma, k_sel);
     if (!ws || ws_bytes < w.total)
       return fail(BSA_ERR_WORKSPACE, "workspace smaller than bsa_workspace_bytes()");
+    // The forward's workspace, when given, still holds the gathered K rows (every key cube) and
+    // Q rows (the query cubes) of these inputs: the backward reads them instead of gathering.
+    const bool reuse = mfma && fwd_ws != nullptr;
+    if (fwd_ws && fwd_ws_bytes < fwd_ws_bytes_min(g, mfma))
+      return fail(BSA_ERR_WORKSPACE, "fwd_ws is smaller than the forward's gathered operands");
     char* base = static_cast<char*>(ws);
     float* delta_c = reinterpret_cast<float*>(base + w.delta);
     float* lse_c = reinterpret_cast<float*>(base + w.lse);
@@ -335,45 +359,50 @@ bsa_status_t bsa_sparse_attn_bwd(const bsa_problem_t* p, bsa_dtype_t dtype, cons
     const bool bf16 = dtype == BSA_BF16;
     Stages stages(stream);
     float2* ld_c = reinterpret_cast<float2*>(base + w.ld);
-    st = hip_status(launch_delta(g, bf16, o, d_o, lse, delta_c, lse_c, ld_c, stream),
-                    "delta launch");
+    auto at = [&](size_t o2) { return reinterpret_cast<bf16_t*>(base + o2); };
+    if (mfma) {
+      // Delta and the (LSE, Delta) pairs in one pass with the dO gather
+      st = hip_status(launch_delta_gather(g, o, d_o, lse, ld_c, at(w.g_dr), stream),
+                      "delta + dO gather launch");
+    } else {
+      st = hip_status(launch_delta(g, bf16, o, d_o, lse, delta_c, lse_c, ld_c, stream),
+                      "delta launch");
+    }
     if (st != BSA_OK) return st;
     st = hip_status(launch_csr(g, idx, k_sel, bits, off, list, stream), "csr launch");
     if (st != BSA_OK) return st;
     stages.done("bwd_prep");
     if (mfma) {
-      auto at = [&](size_t o2) { return reinterpret_cast<bf16_t*>(base + o2); };
       const Geom gq = noise_only(g);
-      st = hip_status(launch_gather(gq, q, nullptr, GATHER_ROW, at(w.g_qr), nullptr, stream),
-                      "gather Q");
-      if (st != BSA_OK) return st;
-      st = hip_status(launch_gather(gq, d_o, nullptr, GATHER_ROW, at(w.g_dr), nullptr, stream),
-                      "gather dO");
-      if (st != BSA_OK) return st;
-      st = hip_status(launch_gather(g, k, k_cache, GATHER_ROW, at(w.g_kr), nullptr, stream),
-                      "gather K");
-      if (st != BSA_OK) return st;
+      const bf16_t* q_rows = reinterpret_cast<const bf16_t*>(
+          reuse ? static_cast<const char*>(fwd_ws) + fwd_q_rows_offset(g) : base + w.g_qr);
+      const bf16_t* k_rows = reinterpret_cast<const bf16_t*>(
+          reuse ? static_cast<const char*>(fwd_ws) : base + w.g_kr);
+      if (!reuse) {
+        st = hip_status(launch_gather(gq, q, nullptr, GATHER_ROW, at(w.g_qr), nullptr, stream),
+                        "gather Q");
+        if (st != BSA_OK) return st;
+        st = hip_status(launch_gather(g, k, k_cache, GATHER_ROW, at(w.g_kr), nullptr, stream),
+                        "gather K");
+        if (st != BSA_OK) return st;
+      }
       st = hip_status(launch_gather(g, v, v_cache, GATHER_ROW, at(w.g_vr), nullptr, stream),
                       "gather V");
       if (st != BSA_OK) return st;
-      stages.done("gather_qkv_do");
-      // longest-first dK/dV dispatch; BSA_DKDV_ORDER=0 keeps the fixed order (tuning aid)
-      const char* ord_env = std::getenv("BSA_DKDV_ORDER");
-      int32_t* order = (ord_env && std::atoi(ord_env) == 0)
-                           ? nullptr
-                           : reinterpret_cast<int32_t*>(base + w.order);
-      st = hip_status(launch_bwd_dkdv_mfma(g, at(w.g_kr), at(w.g_vr), at(w.g_qr), at(w.g_dr),
-                                           ld_c, off, list, order, softmax_scale, dk, dv,
-                                           dk_cache, dv_cache, stream),
+      stages.done(reuse ? "bwd_gather_v" : "bwd_gather_qkv");
+      // longest-first dK/dV dispatch unless this thread asked for the fixed order
+      int32_t* order = t_dkdv_order ? reinterpret_cast<int32_t*>(base + w.order) : nullptr;
+      st = hip_status(launch_bwd_dkdv_mfma(g, k_rows, at(w.g_vr), q_rows, at(w.g_dr), ld_c,
+                                           off, list, order, softmax_scale, dk, dv, dk_cache,
+                                           dv_cache, stream),
                       "dK/dV launch");
       if (st != BSA_OK) return st;
       stages.done("bwd_dkdv_mfma");
-      // software-pipelined dQ where it is faster; BSA_DQ_PIPELINE=0 keeps the plain loop
-      // (same bits; tuning aid)
-      const char* pipe_env = std::getenv("BSA_DQ_PIPELINE");
-      const bool pipelined = !(pipe_env && std::atoi(pipe_env) == 0);
-      st = hip_status(launch_bwd_dq_mfma(g, at(w.g_qr), at(w.g_dr), at(w.g_kr), at(w.g_vr),
-                                         ld_c, idx, k_sel, softmax_scale, dq, pipelined, stream),
+      // software-pipelined dQ where it is faster, unless this thread asked for the plain loop
+      // (same bits)
+      const bool pipelined = t_dq_pipeline != 0;
+      st = hip_status(launch_bwd_dq_mfma(g, q_rows, at(w.g_dr), k_rows, at(w.g_vr), ld_c, idx,
+                                         k_sel, softmax_scale, dq, pipelined, stream),
                       "dQ launch");
       stages.done("bwd_dq_mfma");
     } else {
@@ -385,6 +414,93 @@ bsa_status_t bsa_sparse_attn_bwd(const bsa_problem_t* p, bsa_dtype_t dtype, cons
                                          softmax_scale, dq, stream), "dQ launch");
       stages.done("bwd_dq_simt");
     }
+    return st;
+  });
+}
+
+bsa_status_t bsa_validate_idx(const bsa_problem_t* p, const int32_t* idx, int32_t k_sel,
+                              int32_t* bad_rows, hipStream_t stream) {
+  return guarded([&]() -> bsa_status_t {
+    Geom g;
+    bsa_status_t st = check_problem(p, &g);
+    if (st != BSA_OK) return st;
+    if ((st = check_ksel(g, k_sel)) != BSA_OK) return st;
+    if (!idx || !bad_rows) return fail(BSA_ERR_INVALID_ARG, "idx and bad_rows must be non-NULL");
+    Stages stages(stream);
+    st = hip_status(launch_validate_idx(g, idx, k_sel, bad_rows, stream), "validate launch");
+    stages.done("validate_idx");
+    return st;
+  });
+}
+
+bsa_status_t bsa_set_tuning(bsa_tune_t key, int32_t value) {
+  switch (key) {
+    case BSA_TUNE_FWD_SPLITS:
+      if (value != -1 && (value < 1 || value > kMaxFwdSplits))
+        return fail(BSA_ERR_INVALID_ARG, "forward splits must be -1 (automatic) or 1..64");
+      t_fwd_splits = value;
+      return BSA_OK;
+    case BSA_TUNE_DKDV_ORDER:
+      if (value != 0 && value != 1) return fail(BSA_ERR_INVALID_ARG, "dK/dV order must be 0 or 1");
+      t_dkdv_order = value;
+      return BSA_OK;
+    case BSA_TUNE_DQ_PIPELINE:
+      if (value != 0 && value != 1) return fail(BSA_ERR_INVALID_ARG, "dQ pipeline must be 0 or 1");
+      t_dq_pipeline = value;
+      return BSA_OK;
+  }
+  return fail(BSA_ERR_INVALID_ARG, "unknown tuning key");
+}
+
+int32_t bsa_get_tuning(bsa_tune_t key) {
+  switch (key) {
+    case BSA_TUNE_FWD_SPLITS: return t_fwd_splits;
+    case BSA_TUNE_DKDV_ORDER: return t_dkdv_order;
+    case BSA_TUNE_DQ_PIPELINE: return t_dq_pipeline;
+  }
+  return INT32_MIN;
+}
+
+bsa_status_t bsa_probe_mfma(const void* operands, size_t operand_bytes, int32_t waves,
+                            int32_t iters, float* sink, size_t sink_bytes, hipStream_t stream) {
+  return guarded([&]() -> bsa_status_t {
+    if (!operands || !sink) return fail(BSA_ERR_INVALID_ARG, "operands and sink must be non-NULL");
+    if (operand_bytes < 8192) return fail(BSA_ERR_INVALID_ARG, "operands must hold 8192 bytes");
+    if (waves < 1 || waves > (1 << 22) || iters < 1)
+      return fail(BSA_ERR_INVALID_ARG, "waves must be in 1..2^22 and iters >= 1");
+    if (sink_bytes < (size_t)waves * 64 * sizeof(float))
+      return fail(BSA_ERR_INVALID_ARG, "sink must hold 64 floats per wave");
+    Stages stages(stream);
+    const bsa_status_t st = hip_status(
+        launch_mfma_probe(static_cast<const bf16_t*>(operands), waves, iters, sink, stream),
+        "MFMA probe launch");
+    stages.done("probe_mfma");
+    return st;
+  });
+}
+
+bsa_status_t bsa_probe_tile_read(const void* buf, size_t buf_bytes, int32_t tile_bytes,
+                                 const int32_t* ids, size_t n_ids, int32_t waves,
+                                 int32_t tiles_per_wave, uint32_t* sink, size_t sink_bytes,
+                                 hipStream_t stream) {
+  return guarded([&]() -> bsa_status_t {
+    if (!buf || !ids || !sink) return fail(BSA_ERR_INVALID_ARG, "buf, ids and sink must be non-NULL");
+    if (tile_bytes < 8192 || tile_bytes % 8192 || tile_bytes > (1 << 20))
+      return fail(BSA_ERR_INVALID_ARG, "tile_bytes must be a multiple of 8192, at most 1 MiB");
+    if (buf_bytes < (size_t)tile_bytes || buf_bytes > 0x7fffffffu)
+      return fail(BSA_ERR_INVALID_ARG, "buf must hold one tile and at most 2^31-1 bytes");
+    if (waves < 1 || waves > (1 << 22) || tiles_per_wave < 1)
+      return fail(BSA_ERR_INVALID_ARG, "waves must be in 1..2^22 and tiles_per_wave >= 1");
+    if (n_ids < (size_t)waves * (size_t)tiles_per_wave)
+      return fail(BSA_ERR_INVALID_ARG, "ids must hold waves * tiles_per_wave entries");
+    if (sink_bytes < (size_t)waves * 64 * sizeof(uint32_t))
+      return fail(BSA_ERR_INVALID_ARG, "sink must hold 64 words per wave");
+    Stages stages(stream);
+    const bsa_status_t st = hip_status(
+        launch_tile_read(static_cast<const bf16_t*>(buf), buf_bytes, tile_bytes, ids, waves,
+                         tiles_per_wave, sink, stream),
+        "tile read probe launch");
+    stages.done("probe_tile_read");
     return st;
   });
 }

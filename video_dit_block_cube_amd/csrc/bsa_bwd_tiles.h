@@ -34,32 +34,49 @@ __device__ __forceinline__ void zero16(f32x16& a) {
 
 // ---------------------------------------------------------------------------------------------
 // Shared LDS helpers.
+//
+// A staged ROW half block keeps the D/16 steps of the global layout (1 KB each: lane l's 16 bytes
+// at l*16) but places step s' at s' * kStageStep in LDS, 64 bytes further apart than in memory.
+// The transposed reads take 8-byte runs from four different steps at once; with the steps exactly
+// 1 KB apart those runs fall on the same LDS banks (2- to 4-way conflicts), with the 64-byte skew
+// they cover every bank once.  A byte of the staged block: s' * kStageStep + lane' * 16 + e' * 2
+// for ROW element (step s', lane' = (d / (D/2)) * 32 + row, e' = d % 8).
 // ---------------------------------------------------------------------------------------------
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) char lds_char;
 
+constexpr int kStageStep = 1024 + 64;
+// LDS bytes of one staged 32-row half block.
+template <int D>
+__host__ __device__ constexpr int staged_half_bytes() {
+  return (D / 16) * kStageStep;
+}
+__device__ __forceinline__ constexpr int stage_off(int step, int lane_row, int elem) {
+  return step * kStageStep + lane_row * 16 + elem * 2;
+}
+
 // Operand fragment of a ROW-layout 32-row half block staged in LDS: lane's 16 bytes of step s.
 __device__ __forceinline__ bf16x8 lds_row_frag(const lds_char* stage, int lane, int s) {
-  return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(stage + (s * 64 + lane) * 16);
+  return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(
+      stage + stage_off(s, lane, 0));
 }
 
 // Byte offset (inside a staged ROW half block) of lane's transposed read for operand (db, s2),
 // half eh: ds_read_b64_tr_b16 gives lane m of each 16-lane group g element k of
 // v[4k + m/4][m%4], where v[n] is the 4-element run at lane n's address.  Pointing lane n at
 // row 16*s2 + 8*eh + 4*(g/2) + n/4, columns d = 32*db + 16*(g%2) + 4*(n%4) .. +3 turns the run
-// into the TRANS operand (lane = d, 8 rows in accumulator-row order).
+// into the TRANS operand (lane = d, 8 rows in accumulator-row order).  In ROW terms the lane
+// part is step 2*(g%2) + (n%4)/2, lane' 4*(g/2) + n/4, element 4*(n%2).
 __device__ __forceinline__ int tr_lane_base(int lane) {
   const int g = lane >> 4, n = lane & 15;
-  // ROW element (row r, column d) sits at ((s'*64 + lane')*8 + e')*2 with lane' = (d/64)*32 + r,
-  // s' = (d%64)/8, e' = d%8; the lane-dependent part:
-  return ((128 * (g & 1) + 64 * ((n & 3) >> 1) + 4 * (g >> 1) + (n >> 2)) * 8 + 4 * (n & 1)) * 2;
+  return stage_off(2 * (g & 1) + ((n & 3) >> 1), 4 * (g >> 1) + (n >> 2), 4 * (n & 1));
 }
 // The row-split point of the ROW layout is d = D/2: column d lives at lane' = (d/(D/2))*32 + r,
 // step s' = (d%(D/2))/8.  With d = 32*db + (lane part), that gives per-(db, s2, eh) constants:
 template <int D>
 __device__ __forceinline__ int tr_const(int db, int s2, int eh) {
-  if constexpr (D == 128) return ((256 * (db & 1) + 32 * (db >> 1) + 16 * s2 + 8 * eh) * 8) * 2;
-  else return ((32 * db + 16 * s2 + 8 * eh) * 8) * 2;  // D == 64
+  if constexpr (D == 128) return stage_off(4 * (db & 1), 32 * (db >> 1) + 16 * s2 + 8 * eh, 0);
+  else return stage_off(0, 32 * db + 16 * s2 + 8 * eh, 0);  // D == 64
 }
 template <int D>
 __device__ __forceinline__ bf16x8 lds_trans_frag(const lds_char* stage, int lane_base, int db,
@@ -79,11 +96,21 @@ __device__ __forceinline__ bf16x8 lds_trans_frag(const lds_char* stage, int lane
 // ---------------------------------------------------------------------------------------------
 typedef float f32x4v __attribute__((ext_vector_type(4)));
 
-// Byte offset inside a ROW half block of the 16-byte fragment holding row r0 + lane%16, columns
-// 32*s + 8*(lane/16) .. +7: lane part and (s, r0) part.
-__device__ __forceinline__ int row16_lane(int lane) { return ((lane >> 4) * 64 + (lane & 15)) * 16; }
+// Byte offset inside a staged ROW half block of the 16-byte fragment holding row r0 + lane%16,
+// columns 32*s + 8*(lane/16) .. +7: lane part (step lane/16, lane' lane%16) and (s, r0) part.
+__device__ __forceinline__ int row16_lane(int lane) { return stage_off(lane >> 4, lane & 15, 0); }
 template <int D>
 __device__ __forceinline__ int row16_const(int s, int r0) {
+  return stage_off(((32 * s) % (D / 2)) / 8, ((32 * s) / (D / 2)) * 32 + r0, 0);
+}
+
+// The same fragment in the gathered ROW layout in memory (steps 1 KB apart), for loads straight
+// into registers.
+__device__ __forceinline__ int row16_lane_mem(int lane) {
+  return ((lane >> 4) * 64 + (lane & 15)) * 16;
+}
+template <int D>
+__device__ __forceinline__ int row16_const_mem(int s, int r0) {
   return ((((32 * s) % (D / 2)) / 8) * 64 + ((32 * s) / (D / 2)) * 32 + r0) * 16;
 }
 
@@ -92,12 +119,12 @@ __device__ __forceinline__ int row16_const(int s, int r0) {
 // pointing rule as lds_trans_frag with the row index 8*(g/2) + 4*eh + n/4).
 __device__ __forceinline__ int tr16_lane(int lane) {
   const int g = lane >> 4, n = lane & 15;
-  return ((128 * (g & 1) + 64 * ((n & 3) >> 1) + 8 * (g >> 1) + (n >> 2)) * 8 + 4 * (n & 1)) * 2;
+  return stage_off(2 * (g & 1) + ((n & 3) >> 1), 8 * (g >> 1) + (n >> 2), 4 * (n & 1));
 }
 template <int D>
 __device__ __forceinline__ int tr16_const(int db, int sub, int eh) {
-  if constexpr (D == 128) return ((256 * (db & 1) + 32 * (db >> 1) + 16 * sub + 4 * eh) * 8) * 2;
-  else return ((32 * db + 16 * sub + 4 * eh) * 8) * 2;  // D == 64
+  if constexpr (D == 128) return stage_off(4 * (db & 1), 32 * (db >> 1) + 16 * sub + 4 * eh, 0);
+  else return stage_off(0, 32 * db + 16 * sub + 4 * eh, 0);  // D == 64
 }
 template <int D>
 __device__ __forceinline__ bf16x8 lds_tr16(const lds_char* stage, int lane_base, int db, int sub) {
@@ -131,14 +158,16 @@ __device__ __forceinline__ bf16x8 acc16_to_b32(const f32x4v& x, const f32x4v& y)
   return __builtin_bit_cast(bf16x8, v);
 }
 
-// One 32-row half block (S*1 KB) of a ROW-gathered tensor -> LDS, no VGPRs in between.
+// One 32-row half block (D/16 steps of 1 KB) of a ROW-gathered tensor -> LDS at the staged
+// layout (steps kStageStep apart), no VGPRs in between.
 template <int D>
 __device__ __forceinline__ void stage_half(__amdgpu_buffer_rsrc_t r, int soff, lds_char* dst,
                                            int lane) {
 #pragma unroll
   for (int s = 0; s < D / 16; ++s)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(dst + s * 1024),
-                                             16, lane * 16, soff + s * 1024, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        r, (__attribute__((address_space(3))) void*)(dst + s * kStageStep), 16, lane * 16,
+        soff + s * 1024, 0, 0);
 }
 
 }  // namespace bsa

@@ -42,9 +42,27 @@ hipError_t launch_bwd_dkdv_simt(const Geom& g, bool bf16, const void* q, const v
 hipError_t launch_delta(const Geom& g, bool bf16, const void* o, const void* d_o,
                         const float* lse, float* delta_c, float* lse_c, float2* ld_c,
                         hipStream_t s);
+// Delta fused with the dO gather (bf16, c == 64): ld_c pairs as above and dO in the ROW layout
+// over the nbq query cubes ([B, Hh, nbq, 64*D]).
+hipError_t launch_delta_gather(const Geom& g, const void* o, const void* d_o, const float* lse,
+                               float2* ld_c, bf16_t* do_row, hipStream_t s);
 size_t csr_bits_words(const Geom& g);
 hipError_t launch_csr(const Geom& g, const int32_t* idx, int k_sel, uint32_t* bits,
                       int32_t* csr_off, int32_t* csr_list, hipStream_t s);
+
+// k_validate.hip: counts the rows of idx ([B, Hh, nbq, k_sel]) with an entry outside [0, nbk) or
+// not strictly above the entry before it; *bad_rows (device) is overwritten with the count.
+hipError_t launch_validate_idx(const Geom& g, const int32_t* idx, int k_sel, int32_t* bad_rows,
+                               hipStream_t s);
+
+// k_probe.hip (diagnostics): back-to-back bf16 MFMA on `waves` one-wave workgroups (operands:
+// 8 x 1 KB of bf16 at `operands`; sink: 64 floats per wave), and whole-tile reads of the tiles
+// listed in ids ([waves, tiles_per_wave] tile numbers of buf; sink: 64 words per wave).
+hipError_t launch_mfma_probe(const bf16_t* operands, int waves, int iters, float* sink,
+                             hipStream_t s);
+hipError_t launch_tile_read(const bf16_t* buf, size_t buf_bytes, int tile_bytes,
+                            const int32_t* ids, int waves, int tiles_per_wave, uint32_t* sink,
+                            hipStream_t s);
 
 // k_gather.hip: cube-major, MFMA-operand-ordered copies of a token tensor (c == 64, bf16).
 //   mode bit 1: "row" layout (lane = token, 8 consecutive d per lane);

@@ -23,8 +23,6 @@
 //  * Work order is head-major (all XCDs work on the same (b, h) at a time, keeping that head's
 //    K/V hot in the shared Infinity Cache) and XCD-aware: workgroup L runs on XCD L%8, which gets
 //    a contiguous run of query cubes of the head (spatial neighbours select similar key cubes).
-#include <cstdlib>
-
 #include "bsa_launch.h"
 
 namespace bsa {
@@ -295,17 +293,23 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 // Split over key ranges: range s holds the s-th of NS contiguous runs of the condition cube ids
 // (`rcc` cubes each) and the s-th of NS runs of the noise cube ids (`rcn` each), so every range
 // carries the same share of the always-selected condition cubes.  Work item (range s, b, h, query
-// cube i) attends only the selected cubes of range s and writes a normalised partial O (bf16,
-// [64][D] row-major) plus its base-2 max and row sum.  Range s runs on XCD s%8, whose L2 then
+// cube i) attends only the selected cubes of range s and writes a normalised partial O plus, per
+// query row, (base-2 max, row sum, scale exponent e).  Range s runs on XCD s%8, whose L2 then
 // only ever holds that range of the head's K/V; the XCD takes its ranges one after the other
 // (s = xcd, xcd + 8, ...), heads in order within each.  A pass with r < 8 ranges deals range
 // x % r to XCD x, so every XCD works and the XCDs holding one range split its query cubes.
+//
+// The partial O is stored as fp16 (11 significant bits, against bf16's 8), scaled by 2^-e with
+// the smallest e >= 0 that keeps the row's largest magnitude at or below 2^15: a convex
+// combination of V rows never exceeds max|V|, so e = 0 unless |V| reaches fp16's range, and the
+// power-of-two scale is exact.  The merge then rounds O once more, to the output's bf16; with
+// bf16 partials the two roundings together could reach 2 * 2^-9 * |O|.
 template <int D, bool EARLY_K, bool RAGGED>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_split_kernel(
     Geom g, const bf16_t* __restrict__ q_row, const bf16_t* __restrict__ krow,
     const bf16_t* __restrict__ vtr, const int32_t* __restrict__ idx, int k_sel, float c_log2,
-    int ns, int rcc, int rcn, const uint2* __restrict__ kmask, bf16_t* __restrict__ o_part,
-    float2* __restrict__ ml_part) {
+    int ns, int rcc, int rcn, const uint2* __restrict__ kmask, uint16_t* __restrict__ o_part,
+    float4* __restrict__ ml_part) {
   constexpr int DB = D / 32;
   constexpr int cube_bytes = 64 * D * 2;
   __shared__ bf16x8 qs[(D / 16) * 2 * 64];
@@ -337,11 +341,11 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   if (hi1 < lo1) hi1 = lo1;  // empty condition run (sr * rcc >= nbc)
   const int n_sel = (hi1 - lo1) + (hi2 - lo2);
   const size_t item = ((size_t)sr * g.B * g.Hh + bh) * g.nbq + i;
-  float2* ml = ml_part + item * 64;
+  float4* ml = ml_part + item * 64;
   if (n_sel == 0) {
     if (hh == 0) {
-      ml[l32] = make_float2(-INFINITY, 0.f);
-      ml[32 + l32] = make_float2(-INFINITY, 0.f);
+      ml[l32] = make_float4(-INFINITY, 0.f, 0.f, 0.f);
+      ml[32 + l32] = make_float4(-INFINITY, 0.f, 0.f, 0.f);
     }
     return;
   }
@@ -357,36 +361,52 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   float l_part[2] = {0.f, 0.f};
   attend_span<D, EARLY_K, RAGGED>(g, qs, rk, rv, irow, 2 * lo1, 2 * (lo1 + n_sel), hi1,
                                   lo2 - hi1, c_log2, kmask, lane, acc, m_run, l_part);
-  bf16_t* op = o_part + item * (64 * D);
+  uint16_t* op = o_part + item * (64 * D);
+  typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     const float l = l_part[qb] + __shfl_xor(l_part[qb], 32, 64);
     const float inv = 1.0f / l;
     const int row = 32 * qb + l32;
+    // the row's largest |O| (its 128 values sit in this lane and the one 32 lanes away)
+    float amax = 0.f;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(acc[db][qb][e]));
+    amax = fmaxf(amax, __shfl_xor(amax, 32, 64)) * inv;
+    int ex;
+    (void)__builtin_frexpf(amax, &ex);  // amax < 2^ex
+    const int sc = ex > 15 ? ex - 15 : 0;
+    const float mul = __builtin_ldexpf(inv, -sc);
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
         const int d = 32 * db + 8 * r4 + 4 * hh;
-        uint32_t w0 = (uint32_t)f32_to_bf16_bits(acc[db][qb][4 * r4 + 0] * inv) |
-                      ((uint32_t)f32_to_bf16_bits(acc[db][qb][4 * r4 + 1] * inv) << 16);
-        uint32_t w1 = (uint32_t)f32_to_bf16_bits(acc[db][qb][4 * r4 + 2] * inv) |
-                      ((uint32_t)f32_to_bf16_bits(acc[db][qb][4 * r4 + 3] * inv) << 16);
-        *reinterpret_cast<uint2*>(op + row * D + d) = make_uint2(w0, w1);
+        const f16x2 h0 = {(_Float16)(acc[db][qb][4 * r4 + 0] * mul),
+                          (_Float16)(acc[db][qb][4 * r4 + 1] * mul)};
+        const f16x2 h1 = {(_Float16)(acc[db][qb][4 * r4 + 2] * mul),
+                          (_Float16)(acc[db][qb][4 * r4 + 3] * mul)};
+        *reinterpret_cast<uint2*>(op + row * D + d) =
+            make_uint2(__builtin_bit_cast(uint32_t, h0), __builtin_bit_cast(uint32_t, h1));
       }
-    if (hh == 0) ml[row] = make_float2(m_run[qb], l);
+    if (hh == 0) ml[row] = make_float4(m_run[qb], l, (float)sc, 0.f);
   }
 }
 
-// Merge of the range partials of one query cube: O = sum_s w_s O_s / sum_s w_s with
-// w_s = l_s * 2^(m_s - M), M = max_s m_s; LSE = (M + log2 sum_s w_s) * ln 2.
+// Merge of the range partials of one query cube: O = sum_s w_s 2^e_s O'_s / sum_s w_s with
+// w_s = l_s * 2^(m_s - M), M = max_s m_s, O'_s the stored fp16 partial; LSE = (M + log2 sum_s
+// w_s) * ln 2.  The ranges are summed in their fixed order, so the result does not depend on
+// which range finished first.
 template <int D>
 __global__ __launch_bounds__(256) void fwd_merge_kernel(Geom g, int ns,
-                                                        const bf16_t* __restrict__ o_part,
-                                                        const float2* __restrict__ ml_part,
+                                                        const uint16_t* __restrict__ o_part,
+                                                        const float4* __restrict__ ml_part,
                                                         bf16_t* __restrict__ o,
                                                         float* __restrict__ lse) {
   constexpr int DQ = D / 4;  // columns per thread
+  typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
   const int i = blockIdx.x;
   const int bh = blockIdx.y;
   const int b = bh / g.Hh, h = bh % g.Hh;
@@ -395,7 +415,7 @@ __global__ __launch_bounds__(256) void fwd_merge_kernel(Geom g, int ns,
   const size_t per_s = (size_t)g.B * g.Hh * g.nbq;
   float M = -INFINITY;
   for (int s = 0; s < ns; ++s) {
-    const float2 v = ml_part[(s * per_s + (size_t)bh * g.nbq + i) * 64 + row];
+    const float4 v = ml_part[(s * per_s + (size_t)bh * g.nbq + i) * 64 + row];
     if (v.y > 0.f) M = fmaxf(M, v.x);
   }
   float acc[DQ];
@@ -404,19 +424,22 @@ __global__ __launch_bounds__(256) void fwd_merge_kernel(Geom g, int ns,
   float Lsum = 0.f;
   for (int s = 0; s < ns; ++s) {
     const size_t item = s * per_s + (size_t)bh * g.nbq + i;
-    const float2 v = ml_part[item * 64 + row];
+    const float4 v = ml_part[item * 64 + row];
     if (!(v.y > 0.f)) continue;
     const float w = v.y * fast_exp2(v.x - M);
     Lsum += w;
-    const uint4* src = reinterpret_cast<const uint4*>(o_part + item * (64 * D) + row * D + part * DQ);
+    const float wo = __builtin_ldexpf(w, (int)v.z);
+    const uint4* src =
+        reinterpret_cast<const uint4*>(o_part + item * (64 * D) + row * D + part * DQ);
 #pragma unroll
     for (int c8 = 0; c8 < DQ / 8; ++c8) {
       const uint4 u = src[c8];
       const uint32_t wd[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        acc[c8 * 8 + 2 * k] = fmaf(w, __uint_as_float(wd[k] << 16), acc[c8 * 8 + 2 * k]);
-        acc[c8 * 8 + 2 * k + 1] = fmaf(w, __uint_as_float(wd[k] & 0xFFFF0000u), acc[c8 * 8 + 2 * k + 1]);
+        const f16x2 hv = __builtin_bit_cast(f16x2, wd[k]);
+        acc[c8 * 8 + 2 * k] = fmaf(wo, (float)hv[0], acc[c8 * 8 + 2 * k]);
+        acc[c8 * 8 + 2 * k + 1] = fmaf(wo, (float)hv[1], acc[c8 * 8 + 2 * k + 1]);
       }
     }
   }
@@ -439,7 +462,7 @@ __global__ __launch_bounds__(256) void fwd_merge_kernel(Geom g, int ns,
 size_t fwd_split_bytes(const Geom& g, int ns) {
   if (ns <= 1) return 0;
   const size_t items = (size_t)ns * g.B * g.Hh * g.nbq;
-  return items * 64 * g.D * sizeof(bf16_t) + items * 64 * sizeof(float2) + 256;
+  return items * 64 * g.D * sizeof(uint16_t) + items * 64 * sizeof(float4) + 256;
 }
 
 size_t fwd_kmask_bytes(const Geom& g) { return g.ragged ? (size_t)g.nbk * sizeof(uint2) : 0; }
@@ -486,8 +509,8 @@ static hipError_t launch_fwd_t(const Geom& g, const bf16_t* q_row, const bf16_t*
   const int rcc = (g.nbc + ns - 1) / ns;
   const int rcn = (g.nbq + ns - 1) / ns;
   const size_t items = (size_t)ns * g.B * g.Hh * g.nbq;
-  bf16_t* o_part = static_cast<bf16_t*>(split_ws);
-  float2* ml_part = reinterpret_cast<float2*>(o_part + items * 64 * g.D);
+  uint16_t* o_part = static_cast<uint16_t*>(split_ws);
+  float4* ml_part = reinterpret_cast<float4*>(o_part + items * 64 * g.D);
   const int passes = (ns + 7) / 8;
   dim3 grid((unsigned)(8 * passes * g.B * g.Hh * g.nbq));
   hipLaunchKernelGGL((fwd_split_kernel<D, EK, RG>), grid, dim3(64), 0, s, g, q_row,
@@ -505,21 +528,15 @@ hipError_t launch_fwd_mfma(const Geom& g, const bf16_t* q_row, const bf16_t* k_r
                            void* o, float* lse, int ns, void* split_ws, uint2* kmask,
                            hipStream_t s) {
   const float c_log2 = scale * kLog2e;
-  // Next-K request right after the S MFMAs needs ~30 more VGPRs; D = 128 has no room for them
-  // at two waves per SIMD, so there it is requested together with V (tuning override:
-  // BSA_FWD_EARLY_K=0/1).
-  const char* env = std::getenv("BSA_FWD_EARLY_K");
-  const bool early = env ? std::atoi(env) != 0 : g.D == 64;
+  // The next K tile is requested right after the S MFMAs at D = 64.  D = 128 requests it with
+  // V after the PV MFMAs: the earlier request needs registers it does not have at two waves per
+  // SIMD (the compiler spills, or, with another scheduler, fits it at no measured gain).
 #define BSA_FWD_CALL(DD, EK)                                                                   \
   (g.ragged ? launch_fwd_t<DD, EK, true>(g, q_row, k_row, v_trans, idx, k_sel, c_log2, o, lse, \
                                          ns, split_ws, kmask, s)                                 \
             : launch_fwd_t<DD, EK, false>(g, q_row, k_row, v_trans, idx, k_sel, c_log2, o, lse, \
                                           ns, split_ws, kmask, s))
-  hipError_t e;
-  if (g.D == 64)
-    e = early ? BSA_FWD_CALL(64, true) : BSA_FWD_CALL(64, false);
-  else
-    e = early ? BSA_FWD_CALL(128, true) : BSA_FWD_CALL(128, false);
+  const hipError_t e = g.D == 64 ? BSA_FWD_CALL(64, true) : BSA_FWD_CALL(128, false);
 #undef BSA_FWD_CALL
   return e;
 }

@@ -37,9 +37,10 @@ __global__ __launch_bounds__(64) void bwd_dq_mfma_kernel(
   constexpr int S = D / 16;
   constexpr int DB = D / 32;
   constexpr int cube_bytes = 64 * D * 2;
-  constexpr int half_bytes = 32 * D * 2;
-  __shared__ __attribute__((aligned(16))) char stage0[2 * half_bytes];  // K rows | V rows
-  __shared__ __attribute__((aligned(16))) char stage1[2 * half_bytes];
+  constexpr int half_bytes = 32 * D * 2;            // a 32-row half block in memory
+  constexpr int lds_half = staged_half_bytes<D>();  // the same block staged in LDS
+  __shared__ __attribute__((aligned(16))) char stage0[2 * lds_half];  // K rows | V rows
+  __shared__ __attribute__((aligned(16))) char stage1[2 * lds_half];
 
   const int L = blockIdx.x;
   const int xcd = L & 7;
@@ -63,7 +64,7 @@ __global__ __launch_bounds__(64) void bwd_dq_mfma_kernel(
   {
     const int off0 = irow[0] * cube_bytes;
     stage_half<D>(rk, off0, st0, lane);
-    stage_half<D>(rv, off0, st0 + half_bytes, lane);
+    stage_half<D>(rv, off0, st0 + lds_half, lane);
   }
 
   // Q and dO rows of this query cube as B operands (lane = query, 8 consecutive d).
@@ -97,7 +98,7 @@ __global__ __launch_bounds__(64) void bwd_dq_mfma_kernel(
     const int tn = t + 1 < ntiles ? t + 1 : t;
     const int noff = irow[tn >> 1] * cube_bytes + (tn & 1) * half_bytes;
     stage_half<D>(rk, noff, nxt, lane);
-    stage_half<D>(rv, noff, nxt + half_bytes, lane);
+    stage_half<D>(rv, noff, nxt + lds_half, lane);
     __builtin_amdgcn_s_waitcnt(0x0f70 | ((2 * S) & 0xf) | (((2 * S) >> 4) << 14));  // vmcnt(2S)
     f32x16 st[2], dpt[2];
     zero16(st[0]); zero16(st[1]); zero16(dpt[0]); zero16(dpt[1]);
@@ -110,7 +111,7 @@ __global__ __launch_bounds__(64) void bwd_dq_mfma_kernel(
       st[1] = mfma32(ka[s], qreg[1][s], st[1]);
     }
 #pragma unroll
-    for (int s = 0; s < S; ++s) ka[s] = lds_row_frag(cur + half_bytes, lane, s);
+    for (int s = 0; s < S; ++s) ka[s] = lds_row_frag(cur + lds_half, lane, s);
 #pragma unroll
     for (int s = 0; s < S; ++s) {
       dpt[0] = mfma32(ka[s], dreg[0][s], dpt[0]);

@@ -28,9 +28,10 @@ __global__ __launch_bounds__(64) void bwd_dq_pipe_kernel(
   constexpr int S = D / 16;
   constexpr int DB = D / 32;
   constexpr int cube_bytes = 64 * D * 2;
-  constexpr int half_bytes = 32 * D * 2;
-  __shared__ __attribute__((aligned(16))) char stage0[2 * half_bytes];  // K rows | V rows
-  __shared__ __attribute__((aligned(16))) char stage1[2 * half_bytes];
+  constexpr int half_bytes = 32 * D * 2;            // a 32-row half block in memory
+  constexpr int lds_half = staged_half_bytes<D>();  // the same block staged in LDS
+  __shared__ __attribute__((aligned(16))) char stage0[2 * lds_half];  // K rows | V rows
+  __shared__ __attribute__((aligned(16))) char stage1[2 * lds_half];
 
   const int L = blockIdx.x;
   const int xcd = L & 7;
@@ -54,7 +55,7 @@ __global__ __launch_bounds__(64) void bwd_dq_pipe_kernel(
   auto stage = [&](int t, lds_char* dst) {  // K and V rows of tile t -> dst
     const int off = irow[t >> 1] * cube_bytes + (t & 1) * half_bytes;
     stage_half<D>(rk, off, dst, lane);
-    stage_half<D>(rv, off, dst + half_bytes, lane);
+    stage_half<D>(rv, off, dst + lds_half, lane);
   };
   stage(0, st0);
 
@@ -97,7 +98,7 @@ __global__ __launch_bounds__(64) void bwd_dq_pipe_kernel(
     }
 #pragma unroll
     for (int s = 0; s < S; ++s) {
-      const bf16x8 va = lds_row_frag(src + half_bytes, lane, s);
+      const bf16x8 va = lds_row_frag(src + lds_half, lane, s);
       dpt[0] = mfma32(va, dreg[0][s], dpt[0]);
       dpt[1] = mfma32(va, dreg[1][s], dpt[1]);
     }

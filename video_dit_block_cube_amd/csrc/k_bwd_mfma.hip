@@ -112,8 +112,9 @@ __global__ __launch_bounds__(64) void bwd_dkdv_mfma_kernel(
   constexpr int S = D / 16;
   constexpr int DB = D / 32;
   constexpr int cube_bytes = 64 * D * 2;
-  constexpr int half_bytes = 32 * D * 2;
-  constexpr int stage_bytes = 2 * half_bytes + 256;  // Q rows | dO rows | 32 (LSE2, Delta) pairs
+  constexpr int half_bytes = 32 * D * 2;              // a 32-row half block in memory
+  constexpr int lds_half = staged_half_bytes<D>();    // the same block staged in LDS
+  constexpr int stage_bytes = 2 * lds_half + 256;     // Q rows | dO rows | 32 (LSE2, Delta) pairs
   __shared__ __attribute__((aligned(16))) char stage0[stage_bytes];
   __shared__ __attribute__((aligned(16))) char stage1[stage_bytes];
 
@@ -148,9 +149,9 @@ __global__ __launch_bounds__(64) void bwd_dkdv_mfma_kernel(
   // stage
   auto stage_step = [&](int i, int qb, lds_char* dst) {
     stage_half<D>(rq, i * cube_bytes + qb * half_bytes, dst, lane);
-    stage_half<D>(rd, i * cube_bytes + qb * half_bytes, dst + half_bytes, lane);
+    stage_half<D>(rd, i * cube_bytes + qb * half_bytes, dst + lds_half, lane);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        rl, (__attribute__((address_space(3))) void*)(dst + 2 * half_bytes), 4, lane * 4,
+        rl, (__attribute__((address_space(3))) void*)(dst + 2 * lds_half), 4, lane * 4,
         (i * 64 + 32 * qb) * (int)sizeof(float2), 0, 0);
   };
   if (nsteps > 0) stage_step(csr_list[beg], 0, st0);
@@ -163,13 +164,15 @@ __global__ __launch_bounds__(64) void bwd_dkdv_mfma_kernel(
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(k_row + bh * kv_elems, (size_t)g.nbk * cube_bytes);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(v_row + bh * kv_elems, (size_t)g.nbk * cube_bytes);
   const int r16 = row16_lane(lane);
+  const int r16m = row16_lane_mem(lane);
   bf16x8 kreg[4 * S4], vreg[4 * S4];
 #pragma unroll
   for (int f = 0; f < 4 * S4; ++f) {
     const int nb = f / S4, s = f % S4;
-    const int soff = j * cube_bytes + (nb >> 1) * half_bytes + row16_const<D>(s, 16 * (nb & 1));
-    kreg[f] = bld16(rk, r16, soff);
-    vreg[f] = bld16(rv, r16, soff);
+    const int soff =
+        j * cube_bytes + (nb >> 1) * half_bytes + row16_const_mem<D>(s, 16 * (nb & 1));
+    kreg[f] = bld16(rk, r16m, soff);
+    vreg[f] = bld16(rv, r16m, soff);
   }
 
   f32x16 acck[DB][2], accv[DB][2];
@@ -184,7 +187,7 @@ __global__ __launch_bounds__(64) void bwd_dkdv_mfma_kernel(
     stage_step(csr_list[beg + (tn >> 1)], tn & 1, nxt);
     __builtin_amdgcn_s_waitcnt(0x0f70 | ((2 * S + 1) & 0xf) | (((2 * S + 1) >> 4) << 14));
     const __attribute__((address_space(3))) f32x4* ldp =
-        (const __attribute__((address_space(3))) f32x4*)(cur + 2 * half_bytes);
+        (const __attribute__((address_space(3))) f32x4*)(cur + 2 * lds_half);
     // two 16-query sub-steps per staged half
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
@@ -217,7 +220,7 @@ __global__ __launch_bounds__(64) void bwd_dkdv_mfma_kernel(
 #pragma unroll
       for (int s = 0; s < S4; ++s) {
         const bf16x8 a = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(
-            cur + half_bytes + r16 + row16_const<D>(s, 16 * sub));
+            cur + lds_half + r16 + row16_const<D>(s, 16 * sub));
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb)
           dp[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, vreg[nb * S4 + s], dp[nb], 0, 0, 0);
@@ -230,7 +233,7 @@ __global__ __launch_bounds__(64) void bwd_dkdv_mfma_kernel(
       for (int kb = 0; kb < 2; ++kb) dsb[kb] = acc16_to_b32(dp[2 * kb], dp[2 * kb + 1]);
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const bf16x8 dt = lds_tr16<D>(cur + half_bytes, trb, db, sub);
+        const bf16x8 dt = lds_tr16<D>(cur + lds_half, trb, db, sub);
         const bf16x8 qt = lds_tr16<D>(cur, trb, db, sub);
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
@@ -309,11 +312,14 @@ bwd_dkdv_pair_kernel(Geom g, const bf16_t* __restrict__ k_row, const bf16_t* __r
   constexpr int S4 = D / 32;
   constexpr int DB = D / 32;
   constexpr int cube_bytes = 64 * D * 2;
-  constexpr int half_bytes = 32 * D * 2;
-  constexpr int stage_bytes = 2 * half_bytes + 512;  // Q | dO | pairs (wave 0) | pairs (wave 1)
+  constexpr int half_bytes = 32 * D * 2;              // a 32-row half block in memory
+  constexpr int lds_half = staged_half_bytes<D>();    // the same block staged in LDS
+  constexpr int stage_bytes = 2 * lds_half + 512;     // Q | dO | pairs (wave 0) | pairs (wave 1)
   __shared__ __attribute__((aligned(16))) char stage0[stage_bytes];
   __shared__ __attribute__((aligned(16))) char stage1[stage_bytes];
-  __shared__ __attribute__((aligned(16))) char xch[2][16 * 64 * 2];  // bf16 P of a sub-step
+  // bf16 P of a sub-step: 8 words per lane as two 16-byte blocks, [block][lane] (lane stride 16
+  // bytes: conflict-free 16-byte accesses)
+  __shared__ __attribute__((aligned(16))) char xch[2][16 * 64 * 2];
 
   int bh, j;
   if (order) {
@@ -339,8 +345,8 @@ bwd_dkdv_pair_kernel(Geom g, const bf16_t* __restrict__ k_row, const bf16_t* __r
       make_rsrc(ld_c + (size_t)bh * g.nbq * 64, (size_t)g.nbq * 64 * sizeof(float2));
   lds_char* st0 = (lds_char*)stage0;
   lds_char* st1 = (lds_char*)stage1;
-  const int own_rows = wave * half_bytes;             // this wave's rows inside a stage
-  const int own_pairs = 2 * half_bytes + 256 * wave;  // this wave's (LSE2, Delta) pairs
+  const int own_rows = wave * lds_half;             // this wave's rows inside a stage
+  const int own_pairs = 2 * lds_half + 256 * wave;  // this wave's (LSE2, Delta) pairs
   auto stage_step = [&](int i, int qb, lds_char* dst) {
     stage_half<D>(rs, i * cube_bytes + qb * half_bytes, dst + own_rows, lane);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -355,12 +361,13 @@ bwd_dkdv_pair_kernel(Geom g, const bf16_t* __restrict__ k_row, const bf16_t* __r
   const __amdgpu_buffer_rsrc_t rkv =
       make_rsrc((wave ? v_row : k_row) + bh * kv_elems, (size_t)g.nbk * cube_bytes);
   const int r16 = row16_lane(lane);
+  const int r16m = row16_lane_mem(lane);
   bf16x8 kv[4 * S4];
 #pragma unroll
   for (int f = 0; f < 4 * S4; ++f) {
     const int nb = f / S4, s = f % S4;
-    kv[f] = bld16(rkv, r16,
-                  j * cube_bytes + (nb >> 1) * half_bytes + row16_const<D>(s, 16 * (nb & 1)));
+    kv[f] = bld16(rkv, r16m,
+                  j * cube_bytes + (nb >> 1) * half_bytes + row16_const_mem<D>(s, 16 * (nb & 1)));
   }
   f32x16 acc[DB][2];  // dV^T (wave 0) or dK^T (wave 1)
 #pragma unroll
@@ -387,8 +394,10 @@ bwd_dkdv_pair_kernel(Geom g, const bf16_t* __restrict__ k_row, const bf16_t* __r
         for (int nb = 0; nb < 4; ++nb)
           sc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, kv[nb * S4 + s], sc[nb], 0, 0, 0);
       }
-      __attribute__((address_space(3))) uint32_t* x =
-          (__attribute__((address_space(3))) uint32_t*)(xch[sub]) + lane * 8;
+      // this lane's 8 words of the exchanged P: words 0-3 at lane*16, words 4-7 at 1024 + lane*16
+      typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+      __attribute__((address_space(3))) u32x4* x =
+          (__attribute__((address_space(3))) u32x4*)(xch[sub]) + lane;
       const int q0 = 16 * sub + 4 * (lane >> 4);  // this lane's first query of the sub-step
       if constexpr (R == 0) {
 #pragma unroll
@@ -397,11 +406,10 @@ bwd_dkdv_pair_kernel(Geom g, const bf16_t* __restrict__ k_row, const bf16_t* __r
 #pragma unroll
           for (int nb = 0; nb < 4; ++nb) sc[nb][i] = fast_exp2(fmaf(sc[nb][i], c_log2, -lv));
         }
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb) {
-          x[2 * nb] = pack_bf16x2(sc[nb][0], sc[nb][1]);
-          x[2 * nb + 1] = pack_bf16x2(sc[nb][2], sc[nb][3]);
-        }
+        x[0] = u32x4{pack_bf16x2(sc[0][0], sc[0][1]), pack_bf16x2(sc[0][2], sc[0][3]),
+                     pack_bf16x2(sc[1][0], sc[1][1]), pack_bf16x2(sc[1][2], sc[1][3])};
+        x[64] = u32x4{pack_bf16x2(sc[2][0], sc[2][1]), pack_bf16x2(sc[2][2], sc[2][3]),
+                      pack_bf16x2(sc[3][0], sc[3][1]), pack_bf16x2(sc[3][2], sc[3][3])};
         bf16x8 pb[2];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) pb[kb] = acc16_to_b32(sc[2 * kb], sc[2 * kb + 1]);
@@ -409,7 +417,7 @@ bwd_dkdv_pair_kernel(Geom g, const bf16_t* __restrict__ k_row, const bf16_t* __r
         if (sub == 0) stage_step(csr_list[beg + (tn >> 1)], tn & 1, nxt);
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          const bf16x8 dt = lds_tr16<D>(cur + half_bytes, trb, db, sub);
+          const bf16x8 dt = lds_tr16<D>(cur + lds_half, trb, db, sub);
 #pragma unroll
           for (int kb = 0; kb < 2; ++kb) acc[db][kb] = mfma32(dt, pb[kb], acc[db][kb]);
         }
@@ -417,9 +425,11 @@ bwd_dkdv_pair_kernel(Geom g, const bf16_t* __restrict__ k_row, const bf16_t* __r
         pair_barrier();
         if (sub == 0) stage_step(csr_list[beg + (tn >> 1)], tn & 1, nxt);
         // dS = P o (dP - Delta) from wave 0's bf16 P (same lane layout as this accumulator)
+        const u32x4 xa = x[0], xb = x[64];
+        const uint32_t xw[8] = {xa[0], xa[1], xa[2], xa[3], xb[0], xb[1], xb[2], xb[3]};
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb) {
-          const uint32_t w0 = x[2 * nb], w1 = x[2 * nb + 1];
+          const uint32_t w0 = xw[2 * nb], w1 = xw[2 * nb + 1];
           const float pv[4] = {__uint_as_float(w0 << 16), __uint_as_float(w0 & 0xffff0000u),
                                __uint_as_float(w1 << 16), __uint_as_float(w1 & 0xffff0000u)};
 #pragma unroll

@@ -193,3 +193,84 @@ hipError_t launch_csr(const Geom& g, const int32_t* idx, int k_sel, uint32_t* bi
 }
 
 }  // namespace bsa
+
+namespace bsa {
+
+// Delta fused with the dO gather (bf16, 64-token cubes): one workgroup per (head, query cube,
+// batch) reads the cube's O and dO token rows once, forms Delta = <dO, O> per token, and writes
+// the dO cube in the ROW gather layout (see k_gather.hip) plus the interleaved (LSE * log2 e,
+// Delta) pairs the MFMA backward kernels read (LSE = +inf, Delta = 0 for a slot outside a ragged
+// grid, so such a row's P is 0).  Saves the separate dO gather's second read of dO.
+template <int D>
+__global__ __launch_bounds__(256) void delta_gather_kernel(Geom g, const bf16_t* __restrict__ o,
+                                                           const bf16_t* __restrict__ d_o,
+                                                           const float* __restrict__ lse,
+                                                           float2* __restrict__ ld_c,
+                                                           bf16_t* __restrict__ do_row) {
+  constexpr int LD = D + 8;      // padded LDS row (elements)
+  constexpr int S = D / 16;
+  constexpr int CPR = D / 8;     // 16-byte chunks per token row
+  constexpr int UNITS = 64 * CPR;
+  __shared__ bf16_t tile[64 * LD];
+  __shared__ float dsum[64];
+  const int h = blockIdx.x;
+  const int i = blockIdx.y;
+  const int b = blockIdx.z;
+  const int tid = threadIdx.x;
+  const int bh = b * g.Hh + h;
+  // 256 threads cover 256 / CPR rows per pass; a row's CPR threads are consecutive lanes
+  for (int u = tid; u < UNITS; u += 256) {
+    const int row = u / CPR, ch = u % CPR;
+    const int tok = cube_token(g, i, row);
+    uint4 dv = make_uint4(0u, 0u, 0u, 0u);
+    float part = 0.f;
+    if (tok >= 0) {
+      const size_t off = bnhd_offset(g, g.Nq, b, tok, h) + ch * 8;
+      dv = *reinterpret_cast<const uint4*>(d_o + off);
+      const uint4 ov = *reinterpret_cast<const uint4*>(o + off);
+      const uint32_t dw[4] = {dv.x, dv.y, dv.z, dv.w};
+      const uint32_t ow[4] = {ov.x, ov.y, ov.z, ov.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        part = fmaf(__uint_as_float(dw[k] << 16), __uint_as_float(ow[k] << 16), part);
+        part = fmaf(__uint_as_float(dw[k] & 0xffff0000u), __uint_as_float(ow[k] & 0xffff0000u),
+                    part);
+      }
+    }
+    *reinterpret_cast<uint4*>(tile + row * LD + ch * 8) = dv;
+#pragma unroll
+    for (int off = CPR >> 1; off > 0; off >>= 1) part += __shfl_xor(part, off, 64);
+    if (ch == 0) dsum[row] = part;
+  }
+  __syncthreads();
+  const size_t blk = ((size_t)bh * g.nbq + i) * (size_t)(64 * D);
+  for (int u = tid; u < UNITS; u += 256) {
+    const int lane = u % 64;
+    const int s = (u / 64) % S;
+    const int rb = u / (64 * S);
+    const int row = 32 * rb + (lane & 31);
+    const int d0 = (lane >> 5) * (D / 2) + 8 * s;
+    *reinterpret_cast<uint4*>(do_row + blk + (size_t)u * 8) =
+        *reinterpret_cast<const uint4*>(tile + row * LD + d0);
+  }
+  if (tid < 64) {
+    const int tok = cube_token(g, i, tid);
+    const float lv = tok >= 0 ? lse[(size_t)bh * g.Nq + tok] : INFINITY;
+    ld_c[((size_t)bh * g.nbq + i) * 64 + tid] = make_float2(lv * kLog2e, tok >= 0 ? dsum[tid] : 0.f);
+  }
+}
+
+hipError_t launch_delta_gather(const Geom& g, const void* o, const void* d_o, const float* lse,
+                               float2* ld_c, bf16_t* do_row, hipStream_t s) {
+  if (g.c != 64) return hipErrorInvalidValue;
+  dim3 grid(g.Hh, g.nbq, g.B);
+  if (g.D == 64)
+    hipLaunchKernelGGL(delta_gather_kernel<64>, grid, dim3(256), 0, s, g, (const bf16_t*)o,
+                       (const bf16_t*)d_o, lse, ld_c, do_row);
+  else
+    hipLaunchKernelGGL(delta_gather_kernel<128>, grid, dim3(256), 0, s, g, (const bf16_t*)o,
+                       (const bf16_t*)d_o, lse, ld_c, do_row);
+  return hipGetLastError();
+}
+
+}  // namespace bsa
