@@ -38,8 +38,9 @@
  *    Faults inside kernels surface, as usual for HIP, at the caller's next synchronisation.
  *    No C++ exception crosses this interface.
  *  Threads.  The library keeps no state between calls other than per-thread settings
- *    (bsa_set_kernel_path, bsa_set_tuning, stage events); concurrent calls on different streams
- *    are safe as long as their output and workspace buffers do not overlap.
+ *    (bsa_set_kernel_path, bsa_set_tuning, stage events) and the static scratch array of the
+ *    allocation-free forward; concurrent calls on different streams are safe as long as their
+ *    output and workspace buffers do not overlap (bsa_sparse_attn_fwd_noalloc: see there).
  */
 #ifndef BSA_H_
 #define BSA_H_
@@ -149,6 +150,23 @@ bsa_status_t bsa_sparse_attn_fwd(const bsa_problem_t* p, bsa_dtype_t dtype, cons
                                  const void* v_cache, const int32_t* idx, int32_t k_sel,
                                  float softmax_scale, void* o, float* lse, void* ws,
                                  size_t ws_bytes, hipStream_t stream);
+
+/* Allocation-free variant of bsa_sparse_attn_fwd, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).  Same
+ * arguments, results and errors as bsa_sparse_attn_fwd without ws / ws_bytes: the workspace is a
+ * static device array of BSA_NOALLOC_SCRATCH_BYTES (256 MiB) that each GPU the library runs on
+ * holds until the process ends.  Problems whose bsa_workspace_bytes(p, dtype, k_sel, 0) exceeds
+ * it return BSA_ERR_WORKSPACE and launch nothing (a single-pass forward, BSA_TUNE_FWD_SPLITS = 1,
+ * needs the least).  No call allocates or frees memory.  Every call on one GPU uses that GPU's one
+ * array and leaves its contents behind (nothing in it has to start at zero): calls that overlap
+ * in time on one GPU (other host threads, other streams) race and must be serialised by the
+ * caller. */
+#define BSA_NOALLOC_SCRATCH_BYTES ((size_t)256 << 20)
+bsa_status_t bsa_sparse_attn_fwd_noalloc(const bsa_problem_t* p, bsa_dtype_t dtype,
+                                         const void* q, const void* k, const void* v,
+                                         const void* k_cache, const void* v_cache,
+                                         const int32_t* idx, int32_t k_sel, float softmax_scale,
+                                         void* o, float* lse, hipStream_t stream);
 
 /* Backward of bsa_sparse_attn_fwd with the selection held constant (the forward and backward
  * both ship, meituan.com talk, section 2.2; training with a condition cache is the continuation

@@ -18,6 +18,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libbsa.so")
 
 BSA_F32, BSA_BF16 = 0, 1
+NOALLOC_SCRATCH_BYTES = 256 << 20     # BSA_NOALLOC_SCRATCH_BYTES of include/bsa.h
 _DTYPES = {torch.float32: BSA_F32, torch.bfloat16: BSA_BF16}
 
 STATUS = {0: "BSA_OK", 1: "BSA_ERR_INVALID_ARG", 2: "BSA_ERR_SHAPE", 3: "BSA_ERR_UNSUPPORTED",
@@ -115,6 +116,8 @@ def lib() -> ctypes.CDLL:
             "bsa_set_tuning": (i32, [i32, i32]),
             "bsa_get_tuning": (i32, [i32]),
             "bsa_validate_idx": (i32, [P, vp, i32, vp, vp]),
+            "bsa_sparse_attn_fwd_noalloc": (i32, [P, i32, vp, vp, vp, vp, vp, vp, i32, f32, vp,
+                                                  vp, vp]),
             "bsa_probe_mfma": (i32, [vp, sz, i32, i32, vp, sz, vp]),
             "bsa_probe_tile_read": (i32, [vp, sz, i32, vp, sz, i32, i32, vp, sz, vp]),
         }
@@ -310,6 +313,27 @@ def bsa_sparse_attn_fwd(p: Problem, q, k, v, idx, k_sel: int, softmax_scale: flo
         _ptr(lse, "lse", (p.batch, p.heads, p.Nq), torch.float32),
         _ptr(ws, "workspace") if ws is not None else None, ctypes.c_size_t(need if ws is None else ws.numel()),
         _stream(q)))
+    return o, lse
+
+
+def bsa_sparse_attn_fwd_noalloc(p: Problem, q, k, v, idx, k_sel: int,
+                                softmax_scale: float | None = None, k_cache=None, v_cache=None,
+                                o=None, lse=None):
+    """bsa_sparse_attn_fwd with the library's static device scratch as workspace (no
+    workspace argument, no allocation inside the call; o and lse must then be given)."""
+    if o is None or lse is None:
+        raise ValueError("the allocation-free forward writes into caller-provided o and lse")
+    scale = 1.0 / math.sqrt(p.head_dim) if softmax_scale is None else float(softmax_scale)
+    shp = (p.batch, p.Nq, p.heads, p.head_dim)
+    shc = (p.batch, p.Nc, p.heads, p.head_dim)
+    dt = q.dtype
+    _check(lib().bsa_sparse_attn_fwd_noalloc(
+        ctypes.byref(p.c_struct()), _dtype_code(q), _ptr(q, "q", shp, dt), _ptr(k, "k", shp, dt),
+        _ptr(v, "v", shp, dt), _ptr(k_cache, "k_cache", shc, dt),
+        _ptr(v_cache, "v_cache", shc, dt),
+        _ptr(idx, "idx", (p.batch, p.heads, p.nbq, k_sel), torch.int32), int(k_sel),
+        ctypes.c_float(scale), _ptr(o, "o", shp, dt),
+        _ptr(lse, "lse", (p.batch, p.heads, p.Nq), torch.float32), _stream(q)))
     return o, lse
 
 

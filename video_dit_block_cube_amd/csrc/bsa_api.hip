@@ -10,6 +10,7 @@
 #include <cstring>
 #include <exception>
 #include <climits>
+#include <mutex>
 #include <string>
 
 #include "bsa.h"
@@ -175,6 +176,41 @@ bsa_status_t guarded(F&& f) {
   }
 }
 
+// Scratch of the allocation-free forward (bsa_sparse_attn_fwd_noalloc): one static device array
+// that every GPU the library runs on holds until the process ends.  Host code never uses its name
+// as an address: the device address is looked up once per device, with that device current, and
+// kept per device.
+constexpr size_t kScratchBytes = BSA_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) char scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+// Device address of `scratch` on the device that `stream` launches to (the current device for
+// the null stream).
+bsa_status_t device_scratch(hipStream_t stream, void** out) {
+  int dev = -1;
+  hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "device of the stream");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(BSA_ERR_UNSUPPORTED, "device ordinals above 63 are not supported");
+  std::call_once(g_scratch_once[dev], [dev]() {
+    int cur = -1;
+    hipError_t e2 = hipGetDevice(&cur);
+    if (e2 == hipSuccess && cur != dev) e2 = hipSetDevice(dev);
+    void* ptr = nullptr;
+    if (e2 == hipSuccess) e2 = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (cur >= 0 && cur != dev) (void)hipSetDevice(cur);
+    g_scratch_err[dev] = e2;
+    g_scratch_ptr[dev] = e2 == hipSuccess ? ptr : nullptr;
+  });
+  if (g_scratch_err[dev] != hipSuccess)
+    return hip_status(g_scratch_err[dev], "address of the static scratch array");
+  *out = g_scratch_ptr[dev];
+  return BSA_OK;
+}
+
 bsa_status_t fwd_impl(const bsa_problem_t* p, bsa_dtype_t dtype, const void* q,
                       const void* k, const void* v, const void* k_cache, const void* v_cache,
                       const int32_t* idx, int32_t k_sel, float softmax_scale, void* o, float* lse,
@@ -311,6 +347,20 @@ bsa_status_t bsa_sparse_attn_fwd(const bsa_problem_t* p, bsa_dtype_t dtype, cons
                                  size_t ws_bytes, hipStream_t stream) {
   return fwd_impl(p, dtype, q, k, v, k_cache, v_cache, idx, k_sel, softmax_scale, o, lse, ws,
                   ws_bytes, stream, "workspace");
+}
+
+bsa_status_t bsa_sparse_attn_fwd_noalloc(const bsa_problem_t* p, bsa_dtype_t dtype,
+                                         const void* q, const void* k, const void* v,
+                                         const void* k_cache, const void* v_cache,
+                                         const int32_t* idx, int32_t k_sel, float softmax_scale,
+                                         void* o, float* lse, hipStream_t stream) {
+  return guarded([&]() -> bsa_status_t {
+    void* scratch_ptr = nullptr;
+    const bsa_status_t st = device_scratch(stream, &scratch_ptr);
+    if (st != BSA_OK) return st;
+    return fwd_impl(p, dtype, q, k, v, k_cache, v_cache, idx, k_sel, softmax_scale, o, lse,
+                    scratch_ptr, kScratchBytes, stream, "the static scratch array");
+  });
 }
 
 bsa_status_t bsa_sparse_attn_bwd(const bsa_problem_t* p, bsa_dtype_t dtype, const void* q,
