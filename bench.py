@@ -272,6 +272,8 @@ def main() -> int:
                     help="skip the 720p-class forward + backward step at head dim 64")
     ap.add_argument("--no-microbench", action="store_true",
                     help="skip the MFMA-rate and tile-read microbenchmarks")
+    ap.add_argument("--only-leg", choices=["480p", "continuation", "ragged", "d64"],
+                    help="run only this extra measurement (no headline step), e.g. to profile it")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -288,6 +290,14 @@ def main() -> int:
     from video_dit_block_cube_amd import bsa, synth
 
     dev = torch.device("cuda:0")
+    if args.only_leg:
+        legs = {"480p": lambda: bench_step(bsa, synth, torch, dev, 5, "480p-class"),
+                "d64": lambda: bench_step(bsa, synth, torch, dev, 3, "720p-class", head_dim=64),
+                "continuation": lambda: bench_continuation(bsa, synth, orc, torch, dev, args),
+                "ragged": lambda: bench_ragged(bsa, synth, torch, dev, args)}
+        log(f"only the {args.only_leg} measurement")
+        print(json.dumps({"leg": args.only_leg, "result": legs[args.only_leg]()}), flush=True)
+        return 0
     w = synth.workload(3, with_grad=True)
     log(f"drawing inputs for {w.name} (seed {1000 + w.number})")
     t0 = time.perf_counter()
