@@ -145,3 +145,54 @@ def torch_fwd_all_rows(op, t, idx_d, scale, chunk_pairs=600_000):
                 out_o[b, rows, h] = o.reshape(-1, D)
                 out_l[b, h, rows] = lse.reshape(-1)
     return out_o, out_l
+
+
+def torch_bwd_all(op, t, idx_d, scale, chunk_pairs=2_000_000):
+    """Every gradient of the sparse backward recomputed on the device with plain torch fp32 ops,
+    for a grid whose sides are cube multiples and no condition frames: per chunk of query cubes,
+    gather the selected key cubes' tokens, form P = exp(S - LSE) and dS = P o (dO V^T - Delta)
+    from the recomputed forward, dQ = scale dS K, and scatter-add scale dS^T Q and P^T dO into
+    the key cubes.  A full-size cross-check of every element of the kernels' gradients, beside the
+    fp64 oracle on sampled cubes.  Returns (dQ, dK, dV) [B, Nq, Hh, D] fp32."""
+    import torch
+    assert op.nbc == 0
+    dev = t["q"].device
+    B, Hh, D, c = op.batch, op.heads, op.head_dim, op.c
+    tok = torch.from_numpy(np.asarray(orc.noise_cube_tokens(op), dtype=np.int64)).to(dev)
+    out = [torch.zeros((B, op.Nq, Hh, D), dtype=torch.float32, device=dev) for _ in range(3)]
+    ks = idx_d.shape[-1]
+    n_chunk = max(1, chunk_pairs // (ks * c))
+    slot = torch.arange(c, device=dev)
+    for b in range(B):
+        for h in range(Hh):
+            q = t["q"][b, :, h].float()[tok]                          # [nbq, c, D]
+            k = t["k"][b, :, h].float()[tok]
+            v = t["v"][b, :, h].float()[tok]
+            do = t["dO"][b, :, h].float()[tok]
+            dk = torch.zeros((op.nbq * c, D), dtype=torch.float32, device=dev)
+            dv = torch.zeros_like(dk)
+            dq = torch.empty((op.nbq, c, D), dtype=torch.float32, device=dev)
+            sel_all = idx_d[b, h].long()
+            for i0 in range(0, op.nbq, n_chunk):
+                i1 = min(op.nbq, i0 + n_chunk)
+                n = i1 - i0
+                sel = sel_all[i0:i1]
+                kt = k[sel].reshape(n, ks * c, D)
+                vt = v[sel].reshape(n, ks * c, D)
+                qi, doi = q[i0:i1].contiguous(), do[i0:i1].contiguous()
+                s = torch.bmm(qi, kt.transpose(1, 2).contiguous()) * scale
+                p = torch.exp(s - torch.logsumexp(s, dim=-1, keepdim=True))
+                o = torch.bmm(p, vt.contiguous())
+                delta = (o * doi).sum(-1, keepdim=True)
+                dp = torch.bmm(doi, vt.transpose(1, 2).contiguous())
+                ds = p * (dp - delta)
+                dq[i0:i1] = scale * torch.bmm(ds, kt.contiguous())
+                rows = (sel[:, :, None] * c + slot).reshape(-1)           # key tokens, cube order
+                dk.index_add_(0, rows, (scale * torch.bmm(ds.transpose(1, 2).contiguous(), qi))
+                              .reshape(-1, D))
+                dv.index_add_(0, rows, torch.bmm(p.transpose(1, 2).contiguous(), doi).reshape(-1, D))
+            flat = tok.reshape(-1)
+            out[0][b, flat, h] = dq.reshape(-1, D)
+            out[1][b, flat, h] = dk
+            out[2][b, flat, h] = dv
+    return tuple(out)

@@ -8,7 +8,7 @@ import pytest
 
 import oracle as orc
 from tests._util import (assert_close, cached_inputs, print_case, sample_rows, scale_of, to_dev,
-                         torch_fwd_all_rows)
+                         torch_bwd_all, torch_fwd_all_rows)
 from video_dit_block_cube_amd import bsa, synth
 
 pytestmark = pytest.mark.gpu
@@ -224,6 +224,38 @@ def test_fwd_full_size_sampled(number):
     assert_close(lse, l_all.cpu().numpy(), "bf16", "LSE (every row)", max_abs=2e-3, rel=1e-5)
 
 
+def test_fwd_720p_split_vs_single_pass():
+    """Precision of the key-range split (8 ranges, fp16 partials with a power-of-two row scale,
+    then the merge) against the single pass on the 720p-class workload, every row of every head
+    against plain torch fp32 arithmetic over the same selection.  Both must meet the bf16 bar, and
+    the split may not lose more than a bf16 rounding step of O over the single pass."""
+    import torch
+    w, x = cached_inputs(3)
+    print_case(f"fwd split vs single {w.name}")
+    p = bsa.Problem(**w.shape_dict)
+    op = orc.Problem(**w.shape_dict)
+    t = {k: to_dev(v, w.dtype) for k, v in x.items()}
+    idx_d = _gpu_selection(w, t, p)
+    ks = orc.num_selected(op, w.r)
+    scale = scale_of(op)
+    o_all, l_all = (a.cpu().numpy() for a in torch_fwd_all_rows(op, t, idx_d, scale))
+    errs = {}
+    for splits in (1, 8):
+        with bsa.tuning(fwd_splits=splits):
+            o, lse = bsa.bsa_sparse_attn_fwd(p, t["q"], t["k"], t["v"], idx_d, ks, scale)
+        torch.cuda.synchronize()
+        o, lse = o.float().cpu().numpy(), lse.cpu().numpy()
+        errs[splits] = (assert_close(o, o_all, "bf16", f"O splits={splits}"),
+                        assert_close(lse, l_all, "bf16", f"LSE splits={splits}", max_abs=2e-3,
+                                     rel=1e-5))
+        print(f"  splits={splits}: O max-abs {errs[splits][0][0]:.3e} rel-L2 "
+              f"{errs[splits][0][1]:.3e}; LSE max-abs {errs[splits][1][0]:.3e} rel-L2 "
+              f"{errs[splits][1][1]:.3e}", flush=True)
+    # one bf16 half-ulp at |O| <= 4 is 2^-7: the split's extra rounding stays inside that
+    assert errs[8][0][0] <= errs[1][0][0] + 2.0 ** -7
+    assert errs[8][0][1] <= 1.5 * errs[1][0][1]
+
+
 BWD_SMALL = [
     (1, (), 2, AUTO),                                                   # tiny fp32 (portable)
     (5, (("batch", 2), ("heads", 2), ("T", 8), ("H", 8), ("W", 16)), 3, AUTO),   # bf16 MFMA
@@ -262,6 +294,19 @@ def test_bwd_small(number, over, r, path):
         assert_close(got.cpu().numpy(), rf, w.dtype, name)
 
 
+def _every_element_bwd(op, t, idx_d, scale, dq, dk, dv):
+    """Every element of the three gradients against plain torch fp32 arithmetic on the device over
+    the same selection (which agrees with the fp64 oracle to ~1e-6 on small grids); prints the
+    measured max-abs and rel-L2 of each."""
+    import torch
+    ref = [a.cpu().numpy() for a in torch_bwd_all(op, t, idx_d, scale)]
+    torch.cuda.synchronize()
+    for name, got, r in (("dQ", dq, ref[0]), ("dK", dk, ref[1]), ("dV", dv, ref[2])):
+        err, rl = assert_close(got, r, "bf16", f"{name} (every element)")
+        print(f"  {name} every element: max-abs {err:.3e} rel-L2 {rl:.3e} (max |ref| "
+              f"{np.abs(r).max():.3e})", flush=True)
+
+
 def test_bwd_full_size_sampled():
     w, x = cached_inputs(5)
     print_case(f"bwd full {w.name}")
@@ -291,6 +336,7 @@ def test_bwd_full_size_sampled():
     dO64 = x["dO"].astype(np.float64)
     np.testing.assert_allclose(dv.sum(axis=1), dO64.sum(axis=1), atol=0.5, rtol=1e-2)
     assert np.abs(dk.astype(np.float64).sum(axis=1)).max() < 0.5
+    _every_element_bwd(op, t, idx_d, scale, dq, dk, dv)
 
 
 def test_bwd_720p_full_size_sampled():
@@ -312,11 +358,13 @@ def test_bwd_720p_full_size_sampled():
     nan = lambda: torch.full(t["q"].shape, float("nan"), dtype=torch.float32, device=t["q"].device)
     dq, dk, dv = bsa.bsa_sparse_attn_bwd(p, t["q"], t["k"], t["v"], o, t["dO"], lse, idx_d, ks,
                                          scale, dq=nan(), dk=nan(), dv=nan())
-    del t, o, lse
+    del o, lse
     idx = idx_d.cpu().numpy()
     dq, dk, dv = (a.cpu().numpy() for a in (dq, dk, dv))
     for name, a in (("dQ", dq), ("dK", dk), ("dV", dv)):
         assert np.isfinite(a).all(), f"{name}: unwritten (NaN) entries"
+    _every_element_bwd(op, t, idx_d, scale, dq, dk, dv)
+    del t
     rows = sample_rows(op, [0, 17, 31], 3, seed=21)
     cols = sample_rows(op, [0, 17, 31], 3, seed=22)
     rq, rk, rv = orc.attn_bwd(x["q"], x["k"], x["v"], x["dO"], idx, op, scale, rows=rows,
