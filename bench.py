@@ -272,7 +272,8 @@ def main() -> int:
                     help="skip the 720p-class forward + backward step at head dim 64")
     ap.add_argument("--no-microbench", action="store_true",
                     help="skip the MFMA-rate and tile-read microbenchmarks")
-    ap.add_argument("--only-leg", choices=["480p", "continuation", "ragged", "d64"],
+    ap.add_argument("--only-leg", choices=["480p", "continuation", "ragged", "d64", "smooth",
+                                           "walk"],
                     help="run only this extra measurement (no headline step), e.g. to profile it")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
@@ -294,7 +295,9 @@ def main() -> int:
         legs = {"480p": lambda: bench_step(bsa, synth, torch, dev, 5, "480p-class"),
                 "d64": lambda: bench_step(bsa, synth, torch, dev, 3, "720p-class", head_dim=64),
                 "continuation": lambda: bench_continuation(bsa, synth, orc, torch, dev, args),
-                "ragged": lambda: bench_ragged(bsa, synth, torch, dev, args)}
+                "ragged": lambda: bench_ragged(bsa, synth, torch, dev, args),
+                "smooth": lambda: bench_smooth(bsa, synth, torch, dev),
+                "walk": lambda: bench_walk(bsa, synth, torch, dev)}
         log(f"only the {args.only_leg} measurement")
         print(json.dumps({"leg": args.only_leg, "result": legs[args.only_leg]()}), flush=True)
         return 0
@@ -697,6 +700,51 @@ def bench_ragged(bsa, synth, torch, dev, args, reps=3):
             # per step (pool runs twice)
             "stages_ms_per_step": {k: round(float(np.sum(v)) / reps, 4) for k, v in stage_ms.items()},
             "note": "pool x2, select, fwd, bwd; partial edge cubes masked in the kernels"}
+
+
+def bench_walk(bsa, synth, torch, dev, reps=3, period_us=600):
+    """The 720p-class backward with the real-time walk phase off, then on (each D = 128 dK/dV and
+    dQ item starts its list at the clock's phase within period_us, so the items running together
+    read neighbouring cubes): how much the backward kernels gain from the extra L2 hits.  Per
+    setting, one untimed call, then reps timed calls (so a counter run over this leg sees the
+    dispatches in that order: off first)."""
+    import numpy as np
+    w = synth.workload(3, with_grad=True)
+    log(f"drawing inputs for {w.name}")
+    x = synth.make_inputs(w)
+    t = {k: torch.from_numpy(v).to(dev).to(torch.bfloat16) for k, v in x.items()}
+    del x
+    p = bsa.Problem(**w.shape_dict)
+    ks = bsa.bsa_num_selected(p, w.r)
+    scale = 1.0 / math.sqrt(p.head_dim)
+    ws_f = torch.empty(bsa.bsa_workspace_bytes(p, torch.bfloat16, ks, False), dtype=torch.uint8,
+                       device=dev)
+    ws_b = torch.empty(bsa.bsa_workspace_bytes(p, torch.bfloat16, ks, True), dtype=torch.uint8,
+                       device=dev)
+    qm = bsa.bsa_block_pool(p, t["q"])
+    km = bsa.bsa_block_pool(p, t["k"])
+    idx, _ = bsa.bsa_select_topr(p, qm, km, w.r, with_mask=False)
+    o, lse = bsa.bsa_sparse_attn_fwd(p, t["q"], t["k"], t["v"], idx, ks, scale, workspace=ws_f)
+    dq = torch.empty(t["q"].shape, dtype=torch.float32, device=dev)
+    dk, dv = torch.empty_like(dq), torch.empty_like(dq)
+    out = {}
+    for label, period in (("off", 0), ("on", period_us)):
+        with bsa.tuning(walk_phase_us=period):
+            evs = [bsa.StageEvents(8) for _ in range(reps + 1)]
+            for ev in evs:
+                with ev:
+                    bsa.bsa_sparse_attn_bwd(p, t["q"], t["k"], t["v"], o, t["dO"], lse, idx, ks,
+                                            scale, dq=dq, dk=dk, dv=dv, workspace=ws_b,
+                                            fwd_workspace=ws_f)
+            torch.cuda.synchronize()
+        stage: dict = {}
+        for ev in evs[1:]:
+            for name, ms in ev.elapsed_all():
+                stage.setdefault(name, []).append(ms)
+        out[label] = {k: round(float(np.median(v)), 4) for k, v in stage.items()}
+    return {"workload": "720p-class backward (B=1, Hh=32, D=128, grid 24x48x80, top-r=144), "
+                        f"walk phase off, then on with a {period_us} us period",
+            "stages_ms": out}
 
 
 def bench_smooth(bsa, synth, torch, dev, reps=3):

@@ -239,11 +239,20 @@ bsa_status_t bsa_set_kernel_path(int32_t path);
  *   BSA_TUNE_DKDV_ORDER   1 (default): dK/dV items longest list first; 0: fixed order.  Same bits.
  *   BSA_TUNE_DQ_PIPELINE  1 (default): software-pipelined dQ where it exists; 0: plain loop.
  *                         Same bits.
+ *   BSA_TUNE_WALK_PHASE   0 (default): every backward work item at D = 128 walks its list of
+ *                         cubes from the first entry.  1..1000000: a period in microseconds;
+ *                         each item of the D = 128 dK/dV and pipelined dQ kernels starts at the
+ *                         entry nearest the phase of the GPU's real-time clock within that
+ *                         period (and wraps), so the items running together read neighbouring
+ *                         cubes and share L2 lines.  A locality experiment: the summation order
+ *                         then depends on timing, so the gradients vary at rounding level from
+ *                         run to run (not deterministic).
  * Returns BSA_ERR_INVALID_ARG (setting unchanged) for an unknown key or an out-of-range value. */
 typedef enum {
   BSA_TUNE_FWD_SPLITS = 0,
   BSA_TUNE_DKDV_ORDER = 1,
-  BSA_TUNE_DQ_PIPELINE = 2
+  BSA_TUNE_DQ_PIPELINE = 2,
+  BSA_TUNE_WALK_PHASE = 3
 } bsa_tune_t;
 bsa_status_t bsa_set_tuning(bsa_tune_t key, int32_t value);
 int32_t bsa_get_tuning(bsa_tune_t key); /* INT32_MIN for an unknown key */

@@ -294,6 +294,34 @@ def test_bwd_small(number, over, r, path):
         assert_close(got.cpu().numpy(), rf, w.dtype, name)
 
 
+@pytest.mark.parametrize("period_us", [1, 37])
+def test_bwd_walk_phase(period_us):
+    """The backward with the real-time walk phase (each D = 128 dK/dV and pipelined dQ item
+    starts its list at a clock-dependent entry and wraps): a different summation order, so
+    gradients within the bf16 bar of the oracle, with and without condition cubes."""
+    w, x = cached_inputs(5, (("heads", 2), ("T", 8), ("H", 16), ("W", 32)))
+    print_case(f"bwd walk phase {period_us} us {w.name}")
+    dO = _dO(w, x)
+    p, op, idx, t = _setup(w, x, 9)
+    t["dO"] = to_dev(dO, w.dtype)
+    ks = orc.num_selected(op, 9)
+    scale = scale_of(op)
+    o, lse = _fwd(p, t, idx, ks, scale)
+    with bsa.tuning(walk_phase_us=period_us):
+        got = bsa.bsa_sparse_attn_bwd(p, t["q"], t["k"], t["v"], o, t["dO"], lse, _idx_dev(idx),
+                                      ks, scale)
+    ref = orc.attn_bwd(x["q"], x["k"], x["v"], dO, idx, op, scale)
+    for name, g, rf in zip(("dQ", "dK", "dV"), got, ref):
+        assert_close(g.cpu().numpy(), rf, w.dtype, name)
+    over = dict(heads=2, T=12, H=8, W=16, cond_T=4)
+    with bsa.tuning(walk_phase_us=period_us):
+        w, x, dO, op, idx, scale, got = _cached_bwd_case(over, 3)
+    ref = orc.attn_bwd(x["q"], x["k"], x["v"], dO, idx, op, scale, k_cache=x["k_cache"],
+                       v_cache=x["v_cache"])
+    for name, g, rf in zip(("dQ", "dK", "dV", "dK_cache", "dV_cache"), got, ref):
+        assert_close(g, rf, "bf16", name + " (cached)")
+
+
 def _every_element_bwd(op, t, idx_d, scale, dq, dk, dv):
     """Every element of the three gradients against plain torch fp32 arithmetic on the device over
     the same selection (which agrees with the fp64 oracle to ~1e-6 on small grids); prints the

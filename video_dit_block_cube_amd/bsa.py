@@ -178,12 +178,13 @@ def bsa_set_kernel_path(path: int) -> None:
     _check(lib().bsa_set_kernel_path(int(path)))
 
 
-BSA_TUNE_FWD_SPLITS, BSA_TUNE_DKDV_ORDER, BSA_TUNE_DQ_PIPELINE = 0, 1, 2
+BSA_TUNE_FWD_SPLITS, BSA_TUNE_DKDV_ORDER, BSA_TUNE_DQ_PIPELINE, BSA_TUNE_WALK_PHASE = 0, 1, 2, 3
 
 
 def bsa_set_tuning(key: int, value: int) -> None:
     """Per-thread tuning switch (see include/bsa.h): forward key-range count (-1 automatic),
-    longest-first dK/dV order, pipelined dQ."""
+    longest-first dK/dV order, pipelined dQ, backward walk-phase period in microseconds (0 off;
+    nondeterministic summation order when on)."""
     _check(lib().bsa_set_tuning(int(key), int(value)))
 
 
@@ -195,7 +196,7 @@ class tuning:
     """Context manager: set tuning switches on this thread, restore them on exit.
     Example: `with bsa.tuning(fwd_splits=1): ...`"""
     _KEYS = {"fwd_splits": BSA_TUNE_FWD_SPLITS, "dkdv_order": BSA_TUNE_DKDV_ORDER,
-             "dq_pipeline": BSA_TUNE_DQ_PIPELINE}
+             "dq_pipeline": BSA_TUNE_DQ_PIPELINE, "walk_phase_us": BSA_TUNE_WALK_PHASE}
 
     def __init__(self, **settings):
         self.settings = {self._KEYS[k]: int(v) for k, v in settings.items()}

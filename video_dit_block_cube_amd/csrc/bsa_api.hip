@@ -31,6 +31,7 @@ thread_local int t_path = 0;
 thread_local int t_fwd_splits = -1;
 thread_local int t_dkdv_order = 1;
 thread_local int t_dq_pipeline = 1;
+thread_local int t_walk_phase_us = 0;
 constexpr int kMaxFwdSplits = 64;
 
 constexpr size_t kAlign = 256;
@@ -442,9 +443,11 @@ bsa_status_t bsa_sparse_attn_bwd(const bsa_problem_t* p, bsa_dtype_t dtype, cons
       stages.done(reuse ? "bwd_gather_v" : "bwd_gather_qkv");
       // longest-first dK/dV dispatch unless this thread asked for the fixed order
       int32_t* order = t_dkdv_order ? reinterpret_cast<int32_t*>(base + w.order) : nullptr;
+      // the real-time walk phase (locality experiment), in ticks of the 100 MHz clock
+      const int walk_ticks = t_walk_phase_us * 100;
       st = hip_status(launch_bwd_dkdv_mfma(g, k_rows, at(w.g_vr), q_rows, at(w.g_dr), ld_c,
-                                           off, list, order, softmax_scale, dk, dv, dk_cache,
-                                           dv_cache, stream),
+                                           off, list, order, softmax_scale, walk_ticks, dk, dv,
+                                           dk_cache, dv_cache, stream),
                       "dK/dV launch");
       if (st != BSA_OK) return st;
       stages.done("bwd_dkdv_mfma");
@@ -452,7 +455,7 @@ bsa_status_t bsa_sparse_attn_bwd(const bsa_problem_t* p, bsa_dtype_t dtype, cons
       // (same bits)
       const bool pipelined = t_dq_pipeline != 0;
       st = hip_status(launch_bwd_dq_mfma(g, q_rows, at(w.g_dr), k_rows, at(w.g_vr), ld_c, idx,
-                                         k_sel, softmax_scale, dq, pipelined, stream),
+                                         k_sel, softmax_scale, dq, pipelined, walk_ticks, stream),
                       "dQ launch");
       stages.done("bwd_dq_mfma");
     } else {
@@ -498,6 +501,11 @@ bsa_status_t bsa_set_tuning(bsa_tune_t key, int32_t value) {
       if (value != 0 && value != 1) return fail(BSA_ERR_INVALID_ARG, "dQ pipeline must be 0 or 1");
       t_dq_pipeline = value;
       return BSA_OK;
+    case BSA_TUNE_WALK_PHASE:
+      if (value < 0 || value > 1000000)
+        return fail(BSA_ERR_INVALID_ARG, "walk phase period must be 0 (off) or 1..1000000 us");
+      t_walk_phase_us = value;
+      return BSA_OK;
   }
   return fail(BSA_ERR_INVALID_ARG, "unknown tuning key");
 }
@@ -507,6 +515,7 @@ int32_t bsa_get_tuning(bsa_tune_t key) {
     case BSA_TUNE_FWD_SPLITS: return t_fwd_splits;
     case BSA_TUNE_DKDV_ORDER: return t_dkdv_order;
     case BSA_TUNE_DQ_PIPELINE: return t_dq_pipeline;
+    case BSA_TUNE_WALK_PHASE: return t_walk_phase_us;
   }
   return INT32_MIN;
 }

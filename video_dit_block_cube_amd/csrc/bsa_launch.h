@@ -95,21 +95,24 @@ size_t fwd_kmask_bytes(const Geom& g);
 // cubes; dK/dV of condition key cubes go to dk_cache / dv_cache ([B, Nc, Hh, D]).
 // pipelined: at D = 128 on a grid without partial cubes, run the software-pipelined variant
 // (same bits; launch_bwd_dq_pipe).
+// walk_ticks > 0 (D = 128 dK/dV and pipelined dQ only): each work item starts its walk over its
+// list at the entry nearest the phase of the 100 MHz real-time clock within that period and
+// wraps (locality experiment; the summation order then depends on timing).  0: from the start.
 hipError_t launch_bwd_dq_mfma(const Geom& g, const bf16_t* q_row, const bf16_t* do_row,
                               const bf16_t* k_row, const bf16_t* v_row, const float2* ld_c,
                               const int32_t* idx, int k_sel, float scale, float* dq,
-                              bool pipelined, hipStream_t s);
+                              bool pipelined, int walk_ticks, hipStream_t s);
 hipError_t launch_bwd_dq_pipe(const Geom& g, const bf16_t* q_row, const bf16_t* do_row,
                               const bf16_t* k_row, const bf16_t* v_row, const float2* ld_c,
                               const int32_t* idx, int k_sel, float scale, float* dq,
-                              hipStream_t s);
+                              int walk_ticks, hipStream_t s);
 // order: dkdv_order_bytes(g) bytes the launch fills with the longest-first item order (null:
 // the fixed XCD-balanced order).
 size_t dkdv_order_bytes(const Geom& g);
 hipError_t launch_bwd_dkdv_mfma(const Geom& g, const bf16_t* k_row, const bf16_t* v_row,
                                 const bf16_t* q_row, const bf16_t* do_row, const float2* ld_c,
                                 const int32_t* csr_off, const int32_t* csr_list, int32_t* order,
-                                float scale, float* dk, float* dv, float* dk_cache,
-                                float* dv_cache, hipStream_t s);
+                                float scale, int walk_ticks, float* dk, float* dv,
+                                float* dk_cache, float* dv_cache, hipStream_t s);
 
 }  // namespace bsa

@@ -174,9 +174,10 @@ __global__ __launch_bounds__(64) void bwd_dq_mfma_kernel(
 hipError_t launch_bwd_dq_mfma(const Geom& g, const bf16_t* q_row, const bf16_t* do_row,
                               const bf16_t* k_row, const bf16_t* v_row, const float2* ld_c,
                               const int32_t* idx, int k_sel, float scale, float* dq,
-                              bool pipelined, hipStream_t s) {
+                              bool pipelined, int walk_ticks, hipStream_t s) {
   if (pipelined && g.D == 128 && !g.ragged)
-    return launch_bwd_dq_pipe(g, q_row, do_row, k_row, v_row, ld_c, idx, k_sel, scale, dq, s);
+    return launch_bwd_dq_pipe(g, q_row, do_row, k_row, v_row, ld_c, idx, k_sel, scale, dq,
+                              walk_ticks, s);
   const int cpx = (g.nbq + 7) / 8;
   dim3 grid((unsigned)(g.B * g.Hh * cpx * 8));
   const float c_log2 = scale * kLog2e;

@@ -24,7 +24,7 @@ __global__ __launch_bounds__(64) void bwd_dq_pipe_kernel(
     Geom g, const bf16_t* __restrict__ q_row, const bf16_t* __restrict__ do_row,
     const bf16_t* __restrict__ k_row, const bf16_t* __restrict__ v_row,
     const float2* __restrict__ ld_c, const int32_t* __restrict__ idx, int k_sel, float scale,
-    float c_log2, int cpx, float* __restrict__ dq) {
+    float c_log2, int cpx, int walk_ticks, float* __restrict__ dq) {
   constexpr int S = D / 16;
   constexpr int DB = D / 32;
   constexpr int cube_bytes = 64 * D * 2;
@@ -50,10 +50,23 @@ __global__ __launch_bounds__(64) void bwd_dq_pipe_kernel(
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(v_row + bh * bh_elems, bh_bytes);
   const int32_t* irow = idx + ((size_t)bh * g.nbq + i) * k_sel;
   const int ntiles = 2 * k_sel;  // even and >= 2
+  // first entry of the walk: 0, or (walk phase) the first selected cube at or past the clock's
+  // phase within the period, the walk wrapping around the row
+  int s0 = 0;
+  if (walk_ticks > 0) {
+    const int phase = (int)((wall_clock64() % (uint64_t)walk_ticks) * (uint64_t)g.nbk /
+                            (uint64_t)walk_ticks);
+    for (int e0 = 0; e0 < k_sel; e0 += 64) {
+      const int e = e0 + lane;
+      s0 += __popcll(__ballot(e < k_sel && irow[e] < phase));
+    }
+    if (s0 >= k_sel) s0 = 0;
+  }
+  auto entry = [&](int e) { return irow[e + s0 < k_sel ? e + s0 : e + s0 - k_sel]; };
   lds_char* st0 = (lds_char*)stage0;
   lds_char* st1 = (lds_char*)stage1;
   auto stage = [&](int t, lds_char* dst) {  // K and V rows of tile t -> dst
-    const int off = irow[t >> 1] * cube_bytes + (t & 1) * half_bytes;
+    const int off = entry(t >> 1) * cube_bytes + (t & 1) * half_bytes;
     stage_half<D>(rk, off, dst, lane);
     stage_half<D>(rv, off, dst + lds_half, lane);
   };
@@ -186,13 +199,13 @@ __global__ __launch_bounds__(64) void bwd_dq_pipe_kernel(
 hipError_t launch_bwd_dq_pipe(const Geom& g, const bf16_t* q_row, const bf16_t* do_row,
                               const bf16_t* k_row, const bf16_t* v_row, const float2* ld_c,
                               const int32_t* idx, int k_sel, float scale, float* dq,
-                              hipStream_t s) {
+                              int walk_ticks, hipStream_t s) {
   if (g.D != 128 || g.ragged || k_sel < 1) return hipErrorInvalidValue;
   const int cpx = (g.nbq + 7) / 8;
   dim3 grid((unsigned)(g.B * g.Hh * cpx * 8));
   const float c_log2 = scale * kLog2e;
   hipLaunchKernelGGL((bwd_dq_pipe_kernel<128>), grid, dim3(64), 0, s, g, q_row, do_row, k_row,
-                     v_row, ld_c, idx, k_sel, scale, c_log2, cpx, dq);
+                     v_row, ld_c, idx, k_sel, scale, c_log2, cpx, walk_ticks, dq);
   return hipGetLastError();
 }
 

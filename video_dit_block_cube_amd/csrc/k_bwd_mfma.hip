@@ -306,8 +306,8 @@ bwd_dkdv_pair_kernel(Geom g, const bf16_t* __restrict__ k_row, const bf16_t* __r
                      const bf16_t* __restrict__ q_row, const bf16_t* __restrict__ do_row,
                      const float2* __restrict__ ld_c, const int32_t* __restrict__ csr_off,
                      const int32_t* __restrict__ csr_list, const int32_t* __restrict__ order,
-                     float scale, float c_log2, int ccx, int ncx, float* __restrict__ dk,
-                     float* __restrict__ dv, float* __restrict__ dk_cache,
+                     float scale, float c_log2, int ccx, int ncx, int walk_ticks,
+                     float* __restrict__ dk, float* __restrict__ dv, float* __restrict__ dk_cache,
                      float* __restrict__ dv_cache) {
   constexpr int S4 = D / 32;
   constexpr int DB = D / 32;
@@ -338,6 +338,24 @@ bwd_dkdv_pair_kernel(Geom g, const bf16_t* __restrict__ k_row, const bf16_t* __r
   const int32_t* offs = csr_off + (size_t)bh * (g.nbk + 1);
   const int beg = offs[j], end = offs[j + 1];
   const int nsteps = 2 * (end - beg);
+  // first entry of the walk: 0, or (walk phase) the first query cube at or past the clock's
+  // phase within the period, read once for both waves, the walk wrapping around the list
+  const int nlist = end - beg;
+  int s0 = 0;
+  if (walk_ticks > 0) {
+    __shared__ int walk_phase;
+    if (threadIdx.x == 0)
+      walk_phase = (int)((wall_clock64() % (uint64_t)walk_ticks) * (uint64_t)g.nbq /
+                         (uint64_t)walk_ticks);
+    __syncthreads();
+    const int phase = walk_phase;
+    for (int e0 = 0; e0 < nlist; e0 += 64) {
+      const int e = e0 + lane;
+      s0 += __popcll(__ballot(e < nlist && csr_list[beg + e] < phase));
+    }
+    if (s0 >= nlist) s0 = 0;
+  }
+  auto entry = [&](int e) { return csr_list[beg + (e + s0 < nlist ? e + s0 : e + s0 - nlist)]; };
   const size_t bh_bytes = (size_t)g.nbq * cube_bytes;
   const size_t bh_elems = (size_t)g.nbq * 64 * D;
   const __amdgpu_buffer_rsrc_t rs = make_rsrc((wave ? do_row : q_row) + bh * bh_elems, bh_bytes);
@@ -353,7 +371,7 @@ bwd_dkdv_pair_kernel(Geom g, const bf16_t* __restrict__ k_row, const bf16_t* __r
         rl, (__attribute__((address_space(3))) void*)(dst + own_pairs), 4, lane * 4,
         (i * 64 + 32 * qb) * (int)sizeof(float2), 0, 0);
   };
-  if (nsteps > 0) stage_step(csr_list[beg], 0, st0);
+  if (nsteps > 0) stage_step(entry(0), 0, st0);
 
   // K (wave 0) or V (wave 1) rows of the key cube: B operands of the 16x16x32 products,
   // kv[nb*S4 + s] = (lane%16 = key of 16-block nb, d = 32s + 8*(lane/16) + 0..7)
@@ -385,15 +403,29 @@ bwd_dkdv_pair_kernel(Geom g, const bf16_t* __restrict__ k_row, const bf16_t* __r
       f32x4v sc[4];
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb) sc[nb] = f32x4v{0.f, 0.f, 0.f, 0.f};
+      // Operand reads are issued ahead of their products, so the LDS latency overlaps other
+      // work: the wave's own row fragments of the sub-step first, and the transposed fragments
+      // of the other wave's rows (dO^T for wave 0, Q^T for wave 1) as soon as they are visible:
+      // at the start of sub-step 1, and right after the barrier in sub-step 0 (the barrier that
+      // follows both waves' waits for this step's rows).
+      bf16x8 ar[S4];
+#pragma unroll
+      for (int s = 0; s < S4; ++s)
+        ar[s] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(
+            cur + own_rows + r16 + row16_const<D>(s, 16 * sub));
+      bf16x8 tf[DB];
+      const lds_char* tsrc = R == 0 ? cur + lds_half : cur;
+      if (sub == 1) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db) tf[db] = lds_tr16<D>(tsrc, trb, db, sub);
+      }
+      __builtin_amdgcn_sched_barrier(0);
       // S = Q K^T (wave 0) or dP = dO V^T (wave 1), from the wave's own staged rows
 #pragma unroll
-      for (int s = 0; s < S4; ++s) {
-        const bf16x8 a = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(
-            cur + own_rows + r16 + row16_const<D>(s, 16 * sub));
+      for (int s = 0; s < S4; ++s)
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb)
-          sc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, kv[nb * S4 + s], sc[nb], 0, 0, 0);
-      }
+          sc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ar[s], kv[nb * S4 + s], sc[nb], 0, 0, 0);
       // this lane's 8 words of the exchanged P: words 0-3 at lane*16, words 4-7 at 1024 + lane*16
       typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
       __attribute__((address_space(3))) u32x4* x =
@@ -414,18 +446,27 @@ bwd_dkdv_pair_kernel(Geom g, const bf16_t* __restrict__ k_row, const bf16_t* __r
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) pb[kb] = acc16_to_b32(sc[2 * kb], sc[2 * kb + 1]);
         pair_barrier();  // P is in LDS; both waves have finished the previous step
-        if (sub == 0) stage_step(csr_list[beg + (tn >> 1)], tn & 1, nxt);
+        if (sub == 0) {
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const bf16x8 dt = lds_tr16<D>(cur + lds_half, trb, db, sub);
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb) acc[db][kb] = mfma32(dt, pb[kb], acc[db][kb]);
+          for (int db = 0; db < DB; ++db) tf[db] = lds_tr16<D>(tsrc, trb, db, sub);
+          __builtin_amdgcn_sched_barrier(0);
+          stage_step(entry(tn >> 1), tn & 1, nxt);
         }
+        // dV^T += dO^T P
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb) acc[db][kb] = mfma32(tf[db], pb[kb], acc[db][kb]);
       } else {
         pair_barrier();
-        if (sub == 0) stage_step(csr_list[beg + (tn >> 1)], tn & 1, nxt);
-        // dS = P o (dP - Delta) from wave 0's bf16 P (same lane layout as this accumulator)
+        if (sub == 0) {
+#pragma unroll
+          for (int db = 0; db < DB; ++db) tf[db] = lds_tr16<D>(tsrc, trb, db, sub);
+        }
         const u32x4 xa = x[0], xb = x[64];
+        __builtin_amdgcn_sched_barrier(0);
+        if (sub == 0) stage_step(entry(tn >> 1), tn & 1, nxt);
+        // dS = P o (dP - Delta) from wave 0's bf16 P (same lane layout as this accumulator)
         const uint32_t xw[8] = {xa[0], xa[1], xa[2], xa[3], xb[0], xb[1], xb[2], xb[3]};
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb) {
@@ -438,12 +479,11 @@ bwd_dkdv_pair_kernel(Geom g, const bf16_t* __restrict__ k_row, const bf16_t* __r
         bf16x8 dsb[2];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) dsb[kb] = acc16_to_b32(sc[2 * kb], sc[2 * kb + 1]);
+        // dK^T += Q^T dS
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const bf16x8 qt = lds_tr16<D>(cur, trb, db, sub);
+        for (int db = 0; db < DB; ++db)
 #pragma unroll
-          for (int kb = 0; kb < 2; ++kb) acc[db][kb] = mfma32(qt, dsb[kb], acc[db][kb]);
-        }
+          for (int kb = 0; kb < 2; ++kb) acc[db][kb] = mfma32(tf[db], dsb[kb], acc[db][kb]);
       }
     }
   };
@@ -490,8 +530,8 @@ size_t dkdv_order_bytes(const Geom& g) {
 hipError_t launch_bwd_dkdv_mfma(const Geom& g, const bf16_t* k_row, const bf16_t* v_row,
                                 const bf16_t* q_row, const bf16_t* do_row, const float2* ld_c,
                                 const int32_t* csr_off, const int32_t* csr_list, int32_t* order,
-                                float scale, float* dk, float* dv, float* dk_cache,
-                                float* dv_cache, hipStream_t s) {
+                                float scale, int walk_ticks, float* dk, float* dv,
+                                float* dk_cache, float* dv_cache, hipStream_t s) {
   const int ccx = (g.nbc + 7) / 8, ncx = (g.nbq + 7) / 8;
   dim3 grid((unsigned)(g.B * g.Hh * (ccx + ncx) * 8));
   const float c_log2 = scale * kLog2e;
@@ -509,8 +549,8 @@ hipError_t launch_bwd_dkdv_mfma(const Geom& g, const bf16_t* k_row, const bf16_t
                        dk_cache, dv_cache);
   else
     hipLaunchKernelGGL(bwd_dkdv_pair_kernel<128>, grid, dim3(128), 0, s, g, k_row, v_row, q_row,
-                       do_row, ld_c, csr_off, csr_list, order, scale, c_log2, ccx, ncx, dk, dv,
-                       dk_cache, dv_cache);
+                       do_row, ld_c, csr_off, csr_list, order, scale, c_log2, ccx, ncx, walk_ticks,
+                       dk, dv, dk_cache, dv_cache);
   return hipGetLastError();
 }
 
