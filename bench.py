@@ -445,7 +445,7 @@ def main() -> int:
     if not args.no_continuation:
         out["continuation_fwd"] = bench_continuation(bsa, synth, orc, torch, dev, args)
     if not args.no_dense:
-        out["dense_vs_bsa_fwd"] = bench_dense(bsa, synth, torch, dev, t)
+        out["dense_vs_bsa"] = bench_dense(bsa, synth, torch, dev, t)
     if not args.no_prologue:
         out["qk_prologue"] = bench_prologue(bsa, torch, dev, p)
     if not args.no_ragged:
@@ -545,7 +545,9 @@ def bench_continuation(bsa, synth, orc, torch, dev, args):
 
 
 def _time_fwd(bsa, torch, p, t, r, reps=3):
-    """Pool, select (r) and then the forward alone, timed per stage with HIP events."""
+    """Pool, select (r), then the forward alone and (when t holds dO) the backward reusing the
+    forward's gathers, each timed per stage with HIP events.  Returns (k_sel, forward ms,
+    backward ms or None)."""
     import numpy as np
     ks = bsa.bsa_num_selected(p, r)
     scale = 1.0 / math.sqrt(p.head_dim)
@@ -564,9 +566,24 @@ def _time_fwd(bsa, torch, p, t, r, reps=3):
             bsa.bsa_sparse_attn_fwd(p, t["q"], t["k"], t["v"], idx, ks, scale, o=o, lse=lse,
                                     workspace=ws)
     torch.cuda.synchronize()
-    tot = [sum(ms for _, ms in ev.elapsed_all()) for ev in evs]
+    fwd = float(np.median([sum(ms for _, ms in ev.elapsed_all()) for ev in evs]))
+    bwd = None
+    if "dO" in t:
+        wsb = torch.empty(bsa.bsa_workspace_bytes(p, torch.bfloat16, ks, True), dtype=torch.uint8,
+                          device=t["q"].device)
+        dq = torch.empty(t["q"].shape, dtype=torch.float32, device=t["q"].device)
+        dk, dv = torch.empty_like(dq), torch.empty_like(dq)
+        evs = [bsa.StageEvents(8) for _ in range(reps + 1)]
+        for ev in evs:
+            with ev:
+                bsa.bsa_sparse_attn_bwd(p, t["q"], t["k"], t["v"], o, t["dO"], lse, idx, ks,
+                                        scale, dq=dq, dk=dk, dv=dv, workspace=wsb,
+                                        fwd_workspace=ws)
+        torch.cuda.synchronize()
+        bwd = float(np.median([sum(ms for _, ms in ev.elapsed_all()) for ev in evs[1:]]))
+        del wsb, dq, dk, dv
     del ws, idx
-    return ks, float(np.median(tot))
+    return ks, fwd, bwd
 
 
 def bench_step(bsa, synth, torch, dev, number, label, reps=5, **over):
@@ -870,21 +887,23 @@ def bench_prologue(bsa, torch, dev, p, reps=5):
 
 def bench_dense(bsa, synth, torch, dev, t720):
     """Dense 3D attention (r = all key cubes, the same kernels) against BSA at the 480p- and
-    720p-class grids: forward ms (gathers + attention) and the BSA speedup."""
+    720p-class grids: forward ms (gathers + attention), backward ms (reusing the forward's
+    gathers), and the BSA speedups of the forward and of the training pair (forward + backward).
+    Pool and select are not counted on either side."""
     res = {}
     for number in (2, 3):
-        w = synth.workload(number)
+        w = synth.workload(number, with_grad=True)
         if number == 3:
             t = t720
         else:
             log(f"drawing inputs for {w.name}")
             x = synth.make_inputs(w)
             t = {k: torch.from_numpy(v).to(dev).to(torch.bfloat16) for k, v in x.items()
-                 if k in ("q", "k", "v")}
+                 if k in ("q", "k", "v", "dO")}
             del x
         p = bsa.Problem(**w.shape_dict)
-        ks_b, ms_b = _time_fwd(bsa, torch, p, t, w.r)
-        ks_d, ms_d = _time_fwd(bsa, torch, p, t, p.nbq - 1)
+        ks_b, ms_b, bwd_b = _time_fwd(bsa, torch, p, t, w.r)
+        ks_d, ms_d, bwd_d = _time_fwd(bsa, torch, p, t, p.nbq - 1)
         dense_f = 4.0 * p.batch * p.heads * p.Nq * p.Nq * p.head_dim
         tag = "480p" if number == 2 else "720p"
         res[tag] = {"grid": f"{p.T}x{p.H}x{p.W}", "bsa_k_sel": ks_b, "bsa_fwd_ms": round(ms_b, 3),
@@ -892,7 +911,15 @@ def bench_dense(bsa, synth, torch, dev, t720):
                     "dense_tflops": round(dense_f / (ms_d * 1e-3) / 1e12, 1),
                     "dense_frac_peak": round(dense_f / (ms_d * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                     "bsa_speedup": round(ms_d / ms_b, 2)}
-        log(f"dense vs BSA at {tag}: {ms_d:.2f} ms vs {ms_b:.2f} ms")
+        if bwd_b is not None and bwd_d is not None:
+            res[tag].update({"bsa_bwd_ms": round(bwd_b, 3), "dense_bwd_ms": round(bwd_d, 3),
+                             "dense_bwd_tflops_credited": round(
+                                 2.5 * dense_f / (bwd_d * 1e-3) / 1e12, 1),
+                             "bsa_bwd_speedup": round(bwd_d / bwd_b, 2),
+                             "bsa_fwd_bwd_speedup": round((ms_d + bwd_d) / (ms_b + bwd_b), 2)})
+        log(f"dense vs BSA at {tag}: fwd {ms_d:.2f} vs {ms_b:.2f} ms, bwd "
+            f"{bwd_d if bwd_d is not None else float('nan'):.2f} vs "
+            f"{bwd_b if bwd_b is not None else float('nan'):.2f} ms")
     return res
 
 
