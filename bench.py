@@ -120,13 +120,15 @@ def profile_record(stage: str) -> dict:
     return rec
 
 
-def cpu_baseline(x, op, idx, r, budget_s: float = 20.0):
-    """The fp64 oracle, as it is, on the host cores: the tiny workload (256 tokens) end to end,
-    then a bounded sample of the 720p-class step -- query cubes spread evenly over heads 0, 15 and
-    31, forward then backward (every GEMM of the algorithm for each sampled cube's 145 selected
-    pairs; the key gradients are formed but not scattered).  A first batch of 24 cubes measures
-    the oracle's speed, a second batch is sized to fill the time budget; the rate over both is
-    the baseline, and the full step's time at that rate is reported as extrapolated."""
+def cpu_baseline(x, op, r):
+    """The fp64 oracle, as it is, on the host cores (heads are independent, so one head is an
+    exact share of the work):
+      - the 256-token tiny workload in full: pool, select, forward, backward;
+      - its finite-difference check in full: 32 random directions over (q, k, v) and 256 single
+        coordinates, central differences of the forward's loss with the selection held fixed;
+      - every query cube of head 0 of the 720p-class step: pool, select, forward and the full
+        backward (key gradients included).
+    The head's rate is the baseline; 32 heads at that rate are the extrapolated full step."""
     import numpy as np
     import oracle as orc
     from video_dit_block_cube_amd import synth
@@ -137,52 +139,71 @@ def cpu_baseline(x, op, idx, r, budget_s: float = 20.0):
         threads = 1
     # tiny workload in full: pool, select, forward, backward
     w1 = synth.workload(1)
-    x1 = synth.make_inputs(w1)
+    x1 = {k: v.astype(np.float64) for k, v in synth.make_inputs(w1).items()}
     p1 = orc.Problem(**w1.shape_dict)
-    dO1 = np.random.default_rng(1001).standard_normal(x1["q"].shape).astype(np.float32)
+    dO1 = np.random.default_rng(1001).standard_normal(x1["q"].shape)
+    sc1 = 1 / math.sqrt(p1.head_dim)
     t0 = time.perf_counter()
     qm1, km1 = orc.block_pool(x1["q"], p1), orc.block_pool(x1["k"], p1)
     idx1, _ = orc.select_topr(qm1, km1, p1, w1.r)
-    orc.sparse_attn_fwd(x1["q"], x1["k"], x1["v"], None, None, idx1, p1, 1 / math.sqrt(p1.head_dim))
-    orc.attn_bwd(x1["q"], x1["k"], x1["v"], dO1, idx1, p1, 1 / math.sqrt(p1.head_dim))
+    orc.sparse_attn_fwd(x1["q"], x1["k"], x1["v"], None, None, idx1, p1, sc1)
+    g1 = orc.attn_bwd(x1["q"], x1["k"], x1["v"], dO1, idx1, p1, sc1)
     tiny_s = time.perf_counter() - t0
 
-    scale = 1.0 / math.sqrt(op.head_dim)
-    ks = idx.shape[-1]
-    per_cube = 4.0 * op.c * (ks * op.c) * op.head_dim * 3.5   # fwd + bwd (2.5x) per query cube
-    heads = [h for h in (0, 15, 31) if h < op.heads]
-    golden = 0.6180339887498949
-
-    def rows_batch(start, n):
-        # cube positions by a golden-ratio sequence: evenly spread over the grid in any prefix
-        out = []
-        for k in range(start, start + n):
-            out.append((0, heads[k % len(heads)], int(((k // len(heads)) * golden % 1.0) * op.nbq)))
-        return out
-
-    def run(rows):
-        orc.attn_fwd_rows(x["q"], x["k"], x["v"], None, None, idx, op, scale, rows)
-        orc.attn_bwd(x["q"], x["k"], x["v"], x["dO"], idx, op, scale, rows=rows, key_cubes=[])
-
+    # its finite-difference check in full
+    def loss(q, k, v):
+        return float(np.sum(orc.sparse_attn_fwd(q, k, v, None, None, idx1, p1, sc1)[0] * dO1))
+    rng = np.random.default_rng(77)
+    hstep = 1e-5
+    names = ("q", "k", "v")
+    worst = 0.0
     t0 = time.perf_counter()
-    first = rows_batch(0, 24)
-    run(first)
-    t1 = time.perf_counter()
-    per_row = (t1 - t0) / len(first)
-    n2 = max(0, int((budget_s - (t1 - t0)) / max(per_row, 1e-3)))
-    if n2:
-        run(rows_batch(len(first), n2))
-    el = time.perf_counter() - t0
-    n = len(first) + n2
-    rate = per_cube * n / el
-    full_step = 3.5 * 4.0 * op.batch * op.heads * op.Nq * (ks * op.c) * op.head_dim
+    for _ in range(32):
+        dirs = [rng.standard_normal(x1[n].shape) for n in names]
+        fd = (loss(*[x1[n] + hstep * d for n, d in zip(names, dirs)]) -
+              loss(*[x1[n] - hstep * d for n, d in zip(names, dirs)])) / (2 * hstep)
+        an = sum(float(np.sum(g * d)) for g, d in zip(g1, dirs))
+        worst = max(worst, abs(fd - an) / max(1.0, abs(an)))
+    for t in range(256):
+        which = t % 3
+        pos = int(rng.integers(0, x1[names[which]].size))
+        args = [x1[n].copy() for n in names]
+        args[which].ravel()[pos] += hstep
+        lp = loss(*args)
+        args[which].ravel()[pos] -= 2 * hstep
+        fd = (lp - loss(*args)) / (2 * hstep)
+        an = float(g1[which].ravel()[pos])
+        worst = max(worst, abs(fd - an) / max(1.0, abs(an)))
+    fd_s = time.perf_counter() - t0
+
+    # every query cube of head 0 of the 720p-class step
+    one = {k: np.ascontiguousarray(v[:, :, 0:1]) for k, v in x.items() if k in ("q", "k", "v", "dO")}
+    p_h = orc.Problem(batch=op.batch, heads=1, head_dim=op.head_dim, T=op.T, H=op.H, W=op.W,
+                      cube_t=op.cube_t, cube_h=op.cube_h, cube_w=op.cube_w, cond_T=op.cond_T)
+    scale = 1.0 / math.sqrt(op.head_dim)
+    t0 = time.perf_counter()
+    qm, km = orc.block_pool(one["q"], p_h), orc.block_pool(one["k"], p_h)
+    idx, _ = orc.select_topr(qm, km, p_h, r)
+    orc.sparse_attn_fwd(one["q"], one["k"], one["v"], None, None, idx, p_h, scale)
+    orc.attn_bwd(one["q"], one["k"], one["v"], one["dO"], idx, p_h, scale)
+    head_s = time.perf_counter() - t0
+    ks = idx.shape[-1]
+    head_flop = 3.5 * 4.0 * op.batch * op.Nq * (ks * op.c) * op.head_dim   # fwd + 2.5x fwd
+    rate = head_flop / head_s
     return {"value": rate / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"fp64 oracle fwd+bwd of {n} query cubes of the 720p-class step, spread "
-                      f"evenly over heads {heads} (of {op.batch * op.heads * op.nbq} cubes), in "
-                      f"{el:.1f} s; the 256-token tiny workload end to end in {tiny_s:.3f} s; "
-                      f"{len(os.sched_getaffinity(0))} host cores visible, {threads} BLAS threads",
+            "sample": f"fp64 oracle on every query cube ({op.batch * op.nbq}) of head 0 of the "
+                      f"720p-class step: pool, select, forward, backward with key gradients, in "
+                      f"{head_s:.1f} s; the 256-token tiny workload end to end in {tiny_s:.3f} s "
+                      f"and its finite-difference check (32 directions + 256 coordinates) in "
+                      f"{fd_s:.1f} s; {len(os.sched_getaffinity(0))} host cores visible, {threads} "
+                      "BLAS threads",
+            "head_s": round(head_s, 2),
             "tiny_workload_s": round(tiny_s, 4),
-            "extrapolated_720p_step_s": round(full_step / rate, 1)}
+            "tiny_fd_check_s": round(fd_s, 2),
+            "tiny_fd_worst_rel_err": float(f"{worst:.2e}"),
+            "extrapolated_720p_step_s": round(head_s * op.heads, 1),
+            "extrapolated": "extrapolated_720p_step_s = head_s x the 32 heads (heads are "
+                            "independent); value, head_s and the tiny figures are measured"}
 
 
 def bench_microbench(bsa, torch, dev, reps=3):
@@ -466,7 +487,7 @@ def main() -> int:
 
     if not args.no_cpu:
         log("CPU oracle baseline")
-        out["cpu_baseline"] = cpu_baseline(x, op, idx.cpu().numpy(), w.r)
+        out["cpu_baseline"] = cpu_baseline(x, op, w.r)
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)
