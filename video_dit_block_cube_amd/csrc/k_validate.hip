@@ -6,7 +6,7 @@
 // each id to one key cube.  A malformed row would give dQ that disagrees with dK/dV.
 //
 // One wave per row: lane l checks entry l (and l + 64, ...) against its range and against the
-// entry before it; the row's verdict is one ballot, and the first lane of a bad row adds one to
+// entry before it; the row's result is one ballot, and the first lane of a bad row adds one to
 // the counter.
 #include "bsa_launch.h"
 
