@@ -294,7 +294,7 @@ def main() -> int:
     ap.add_argument("--no-microbench", action="store_true",
                     help="skip the MFMA-rate and tile-read microbenchmarks")
     ap.add_argument("--only-leg", choices=["480p", "continuation", "ragged", "d64", "smooth",
-                                           "walk"],
+                                           "walk", "dkdv_split"],
                     help="run only this extra measurement (no headline step), e.g. to profile it")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
@@ -318,7 +318,8 @@ def main() -> int:
                 "continuation": lambda: bench_continuation(bsa, synth, orc, torch, dev, args),
                 "ragged": lambda: bench_ragged(bsa, synth, torch, dev, args),
                 "smooth": lambda: bench_smooth(bsa, synth, torch, dev),
-                "walk": lambda: bench_walk(bsa, synth, torch, dev)}
+                "walk": lambda: bench_walk(bsa, synth, torch, dev),
+                "dkdv_split": lambda: bench_dkdv_split(bsa, synth, torch, dev)}
         log(f"only the {args.only_leg} measurement")
         print(json.dumps({"leg": args.only_leg, "result": legs[args.only_leg]()}), flush=True)
         return 0
@@ -740,12 +741,10 @@ def bench_ragged(bsa, synth, torch, dev, args, reps=3):
             "note": "pool x2, select, fwd, bwd; partial edge cubes masked in the kernels"}
 
 
-def bench_walk(bsa, synth, torch, dev, reps=3, period_us=600):
-    """The 720p-class backward with the real-time walk phase off, then on (each D = 128 dK/dV and
-    dQ item starts its list at the clock's phase within period_us, so the items running together
-    read neighbouring cubes): how much the backward kernels gain from the extra L2 hits.  Per
-    setting, one untimed call, then reps timed calls (so a counter run over this leg sees the
-    dispatches in that order: off first)."""
+def bench_bwd_settings(bsa, synth, torch, dev, settings, reps=3):
+    """The 720p-class backward under each (label, tuning) setting in turn, on the headline step's
+    seeded inputs: per setting one untimed call, then reps timed calls (so a counter run over
+    the leg sees the dispatches in that order)."""
     import numpy as np
     w = synth.workload(3, with_grad=True)
     log(f"drawing inputs for {w.name}")
@@ -766,8 +765,8 @@ def bench_walk(bsa, synth, torch, dev, reps=3, period_us=600):
     dq = torch.empty(t["q"].shape, dtype=torch.float32, device=dev)
     dk, dv = torch.empty_like(dq), torch.empty_like(dq)
     out = {}
-    for label, period in (("off", 0), ("on", period_us)):
-        with bsa.tuning(walk_phase_us=period):
+    for label, tune in settings:
+        with bsa.tuning(**tune):
             evs = [bsa.StageEvents(8) for _ in range(reps + 1)]
             for ev in evs:
                 with ev:
@@ -780,9 +779,26 @@ def bench_walk(bsa, synth, torch, dev, reps=3, period_us=600):
             for name, ms in ev.elapsed_all():
                 stage.setdefault(name, []).append(ms)
         out[label] = {k: round(float(np.median(v)), 4) for k, v in stage.items()}
+    return out
+
+
+def bench_walk(bsa, synth, torch, dev, period_us=600):
+    """The 720p-class backward with the real-time walk phase off, then on (each D = 128 dK/dV and
+    dQ item starts its list at the clock's phase within period_us, so the items running together
+    read neighbouring cubes): how much the backward kernels gain from the extra L2 hits."""
     return {"workload": "720p-class backward (B=1, Hh=32, D=128, grid 24x48x80, top-r=144), "
                         f"walk phase off, then on with a {period_us} us period",
-            "stages_ms": out}
+            "stages_ms": bench_bwd_settings(bsa, synth, torch, dev,
+                                            [("off", {}), ("on", {"walk_phase_us": period_us})])}
+
+
+def bench_dkdv_split(bsa, synth, torch, dev):
+    """The 720p-class backward with the dK/dV work of each key cube split between its two waves
+    by output (default; dK's dS from the bf16 P) and by keys (dS from the fp32 P)."""
+    return {"workload": "720p-class backward (B=1, Hh=32, D=128, grid 24x48x80, top-r=144), "
+                        "dK/dV split by output, then by keys",
+            "stages_ms": bench_bwd_settings(bsa, synth, torch, dev,
+                                            [("by_output", {}), ("by_keys", {"dkdv_split": 1})])}
 
 
 def bench_smooth(bsa, synth, torch, dev, reps=3):

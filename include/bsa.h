@@ -247,12 +247,19 @@ bsa_status_t bsa_set_kernel_path(int32_t path);
  *                         cubes and share L2 lines.  A locality experiment: the summation order
  *                         then depends on timing, so the gradients vary at rounding level from
  *                         run to run (not deterministic).
+ *   BSA_TUNE_DKDV_SPLIT   0 (default): the bf16 MFMA dK/dV at D = 128 splits each key cube's
+ *                         work between two waves by output (one accumulates dV, the other dK,
+ *                         the softmax P crosses between them as bf16, so dK's dS is formed from
+ *                         the bf16-rounded P).  1: by keys (each wave accumulates dK and dV of
+ *                         half the keys and forms dS from its own fp32 P, as the dQ pass does):
+ *                         dK closer to the exact gradient, a few percent slower.
  * Returns BSA_ERR_INVALID_ARG (setting unchanged) for an unknown key or an out-of-range value. */
 typedef enum {
   BSA_TUNE_FWD_SPLITS = 0,
   BSA_TUNE_DKDV_ORDER = 1,
   BSA_TUNE_DQ_PIPELINE = 2,
-  BSA_TUNE_WALK_PHASE = 3
+  BSA_TUNE_WALK_PHASE = 3,
+  BSA_TUNE_DKDV_SPLIT = 4
 } bsa_tune_t;
 bsa_status_t bsa_set_tuning(bsa_tune_t key, int32_t value);
 int32_t bsa_get_tuning(bsa_tune_t key); /* INT32_MIN for an unknown key */

@@ -188,11 +188,13 @@ def test_tuning_switches_are_checked_and_per_thread(L):
     assert bsa.bsa_get_tuning(bsa.BSA_TUNE_DKDV_ORDER) == 1
     assert bsa.bsa_get_tuning(bsa.BSA_TUNE_DQ_PIPELINE) == 1
     assert bsa.bsa_get_tuning(bsa.BSA_TUNE_WALK_PHASE) == 0     # deterministic walk by default
+    assert bsa.bsa_get_tuning(bsa.BSA_TUNE_DKDV_SPLIT) == 0     # split by output by default
     assert L.bsa_get_tuning(7) == -(2 ** 31)
     for key, bad in ((bsa.BSA_TUNE_FWD_SPLITS, 0), (bsa.BSA_TUNE_FWD_SPLITS, 65),
                      (bsa.BSA_TUNE_FWD_SPLITS, -2), (bsa.BSA_TUNE_DKDV_ORDER, 2),
                      (bsa.BSA_TUNE_DQ_PIPELINE, -1), (bsa.BSA_TUNE_WALK_PHASE, -1),
-                     (bsa.BSA_TUNE_WALK_PHASE, 1000001), (9, 1)):
+                     (bsa.BSA_TUNE_WALK_PHASE, 1000001), (bsa.BSA_TUNE_DKDV_SPLIT, 2),
+                     (bsa.BSA_TUNE_DKDV_SPLIT, -1), (9, 1)):
         assert L.bsa_set_tuning(key, bad) == INVALID
     with bsa.tuning(walk_phase_us=600):
         assert bsa.bsa_get_tuning(bsa.BSA_TUNE_WALK_PHASE) == 600

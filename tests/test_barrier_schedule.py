@@ -36,17 +36,27 @@ def _function(asm: str, symbol_prefix: str) -> list:
     return asm[start:end].splitlines()
 
 
-def _loops(lines: list) -> list:
-    """(first, last) line of every loop: a 'Loop Header' label up to the last branch back to it."""
-    loops = []
-    for i, ln in enumerate(lines):
-        m = re.match(r"^(\.LBB\w+):.*Loop Header", ln)
-        if m:
-            back = [j for j, l2 in enumerate(lines)
-                    if j > i and re.search(r"\bs_c?branch\w*\s+" + re.escape(m.group(1)) + r"\b", l2)]
-            if back:
-                loops.append((i, max(back)))
-    return loops
+def _barriers_per_loop(lines: list) -> tuple:
+    """s_barrier count of each loop (innermost, keyed by its header block) and outside every
+    loop, from the assembler's block comments ('Loop Header' / 'in Loop: Header=...')."""
+    per, outside, cur = {}, 0, None
+    for ln in lines:
+        label = re.match(r"^(\.LBB\w+|; %bb\.\d+):", ln)
+        if label:
+            m = re.search(r"in Loop: Header=(BB\w+)", ln)
+            if "Loop Header" in ln:
+                cur = label.group(1).lstrip(".L")
+            elif m:
+                cur = m.group(1)
+            else:
+                cur = None
+            continue
+        if re.match(r"\s*s_barrier\b", ln):
+            if cur is None:
+                outside += 1
+            else:
+                per[cur] = per.get(cur, 0) + 1
+    return per, outside
 
 
 def _barriers(lines: list) -> int:
@@ -56,10 +66,18 @@ def _barriers(lines: list) -> int:
 def test_two_wave_dkdv_roles_meet_the_same_barriers():
     lines = _function(_assembly(os.path.join(B.CSRC, "k_bwd_mfma.hip")),
                       "_ZN3bsa20bwd_dkdv_pair_kernelILi128E")
-    loops = _loops(lines)
-    per_loop = [_barriers(lines[a:b + 1]) for a, b in loops]
-    step_loops = [c for c in per_loop if c > 0]
-    assert len(step_loops) == 2, per_loop                 # one step loop per role
-    assert step_loops[0] == step_loops[1] >= 2, per_loop  # same barriers per iteration
-    outside = _barriers(lines) - sum(step_loops)
-    assert outside == 1, (outside, per_loop)              # the walk-phase broadcast only
+    per, outside = _barriers_per_loop(lines)
+    counts = sorted(per.values())
+    assert len(counts) == 2, per                  # one step loop per role
+    assert counts[0] == counts[1] >= 2, per       # the same barriers per iteration
+    assert outside == 1, (outside, per)           # the walk-phase broadcast only
+
+
+def test_key_split_dkdv_waves_share_one_loop():
+    """The split-by-keys dK/dV runs one loop for both waves: one loop with barriers, the
+    walk-phase broadcast outside it."""
+    lines = _function(_assembly(os.path.join(B.CSRC, "k_bwd_mfma.hip")),
+                      "_ZN3bsa20bwd_dkdv_keys_kernelILi128E")
+    per, outside = _barriers_per_loop(lines)
+    assert len(per) == 1 and min(per.values()) >= 1, per
+    assert outside == 1, (outside, per)

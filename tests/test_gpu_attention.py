@@ -322,6 +322,68 @@ def test_bwd_walk_phase(period_us):
         assert_close(g, rf, "bf16", name + " (cached)")
 
 
+@pytest.mark.parametrize("case", ["plain", "cache", "ragged", "d64"])
+def test_bwd_dkdv_split_by_keys(case):
+    """BSA_TUNE_DKDV_SPLIT = 1 (each wave of a key cube takes half its keys and forms dS from the
+    fp32 P) against the oracle: without and with condition cubes, on a ragged grid, and at
+    D = 64, where the switch changes nothing (the one-wave kernel runs)."""
+    print_case(f"bwd dK/dV split by keys, {case}")
+    if case == "cache":
+        with bsa.tuning(dkdv_split=1):
+            w, x, dO, op, idx, scale, got = _cached_bwd_case(dict(heads=2, T=12, H=8, W=16,
+                                                                  cond_T=4), 3)
+        ref = orc.attn_bwd(x["q"], x["k"], x["v"], dO, idx, op, scale, k_cache=x["k_cache"],
+                           v_cache=x["v_cache"])
+        for name, g, rf in zip(("dQ", "dK", "dV", "dK_cache", "dV_cache"), got, ref):
+            assert_close(g, rf, "bf16", name)
+        return
+    over = {"plain": (("heads", 2), ("T", 8), ("H", 16), ("W", 32)),
+            "ragged": (("heads", 2), ("T", 8), ("H", 14), ("W", 27)),
+            "d64": (("heads", 2), ("head_dim", 64), ("T", 8), ("H", 8), ("W", 16))}[case]
+    w, x = cached_inputs(5, over)
+    dO = _dO(w, x)
+    p, op, idx, t = _setup(w, x, 5)
+    t["dO"] = to_dev(dO, w.dtype)
+    ks = orc.num_selected(op, 5)
+    scale = scale_of(op)
+    o, lse = _fwd(p, t, idx, ks, scale)
+    with bsa.tuning(dkdv_split=1):
+        got = bsa.bsa_sparse_attn_bwd(p, t["q"], t["k"], t["v"], o, t["dO"], lse, _idx_dev(idx),
+                                      ks, scale)
+    ref = orc.attn_bwd(x["q"], x["k"], x["v"], dO, idx, op, scale)
+    for name, g, rf in zip(("dQ", "dK", "dV"), got, ref):
+        assert_close(g.cpu().numpy(), rf, w.dtype, name)
+
+
+def test_bwd_dkdv_split_by_keys_full_size():
+    """The 480p backward with the split by keys, every element against plain torch fp32
+    products: dK's dS now comes from the fp32 P like dQ's, so dK's relative error drops to the
+    level of dQ's and dV's; and two identical calls agree bit for bit."""
+    import torch
+    w, x = cached_inputs(5)
+    print_case(f"bwd dK/dV split by keys, full size {w.name}")
+    p = bsa.Problem(**w.shape_dict)
+    op = orc.Problem(**w.shape_dict)
+    t = {k: to_dev(v, w.dtype) for k, v in x.items()}
+    idx_d = _gpu_selection(w, t, p)
+    ks = orc.num_selected(op, w.r)
+    scale = scale_of(op)
+    o, lse = bsa.bsa_sparse_attn_fwd(p, t["q"], t["k"], t["v"], idx_d, ks, scale)
+    with bsa.tuning(dkdv_split=1):
+        g1 = bsa.bsa_sparse_attn_bwd(p, t["q"], t["k"], t["v"], o, t["dO"], lse, idx_d, ks, scale)
+        g2 = bsa.bsa_sparse_attn_bwd(p, t["q"], t["k"], t["v"], o, t["dO"], lse, idx_d, ks, scale)
+    torch.cuda.synchronize()
+    for a, b_ in zip(g1, g2):
+        assert torch.equal(a, b_)
+    ref = [a.cpu().numpy() for a in torch_bwd_all(op, t, idx_d, scale)]
+    errs = {}
+    for name, g, r in zip(("dQ", "dK", "dV"), g1, ref):
+        errs[name] = assert_close(g.cpu().numpy(), r, "bf16", f"{name} (every element)")
+        print(f"  {name} every element: max-abs {errs[name][0]:.3e} rel-L2 {errs[name][1]:.3e}",
+              flush=True)
+    assert errs["dK"][1] <= 1.2 * max(errs["dQ"][1], errs["dV"][1])
+
+
 def _every_element_bwd(op, t, idx_d, scale, dq, dk, dv):
     """Every element of the three gradients against plain torch fp32 arithmetic on the device over
     the same selection (which agrees with the fp64 oracle to ~1e-6 on small grids); prints the

@@ -178,13 +178,14 @@ def bsa_set_kernel_path(path: int) -> None:
     _check(lib().bsa_set_kernel_path(int(path)))
 
 
-BSA_TUNE_FWD_SPLITS, BSA_TUNE_DKDV_ORDER, BSA_TUNE_DQ_PIPELINE, BSA_TUNE_WALK_PHASE = 0, 1, 2, 3
+(BSA_TUNE_FWD_SPLITS, BSA_TUNE_DKDV_ORDER, BSA_TUNE_DQ_PIPELINE, BSA_TUNE_WALK_PHASE,
+ BSA_TUNE_DKDV_SPLIT) = 0, 1, 2, 3, 4
 
 
 def bsa_set_tuning(key: int, value: int) -> None:
     """Per-thread tuning switch (see include/bsa.h): forward key-range count (-1 automatic),
     longest-first dK/dV order, pipelined dQ, backward walk-phase period in microseconds (0 off;
-    nondeterministic summation order when on)."""
+    nondeterministic summation order when on), dK/dV split by keys (1) instead of by output."""
     _check(lib().bsa_set_tuning(int(key), int(value)))
 
 
@@ -196,7 +197,8 @@ class tuning:
     """Context manager: set tuning switches on this thread, restore them on exit.
     Example: `with bsa.tuning(fwd_splits=1): ...`"""
     _KEYS = {"fwd_splits": BSA_TUNE_FWD_SPLITS, "dkdv_order": BSA_TUNE_DKDV_ORDER,
-             "dq_pipeline": BSA_TUNE_DQ_PIPELINE, "walk_phase_us": BSA_TUNE_WALK_PHASE}
+             "dq_pipeline": BSA_TUNE_DQ_PIPELINE, "walk_phase_us": BSA_TUNE_WALK_PHASE,
+             "dkdv_split": BSA_TUNE_DKDV_SPLIT}
 
     def __init__(self, **settings):
         self.settings = {self._KEYS[k]: int(v) for k, v in settings.items()}

@@ -32,6 +32,7 @@ thread_local int t_fwd_splits = -1;
 thread_local int t_dkdv_order = 1;
 thread_local int t_dq_pipeline = 1;
 thread_local int t_walk_phase_us = 0;
+thread_local int t_dkdv_split = 0;
 constexpr int kMaxFwdSplits = 64;
 
 constexpr size_t kAlign = 256;
@@ -446,8 +447,8 @@ bsa_status_t bsa_sparse_attn_bwd(const bsa_problem_t* p, bsa_dtype_t dtype, cons
       // the real-time walk phase (locality experiment), in ticks of the 100 MHz clock
       const int walk_ticks = t_walk_phase_us * 100;
       st = hip_status(launch_bwd_dkdv_mfma(g, k_rows, at(w.g_vr), q_rows, at(w.g_dr), ld_c,
-                                           off, list, order, softmax_scale, walk_ticks, dk, dv,
-                                           dk_cache, dv_cache, stream),
+                                           off, list, order, softmax_scale, walk_ticks,
+                                           t_dkdv_split != 0, dk, dv, dk_cache, dv_cache, stream),
                       "dK/dV launch");
       if (st != BSA_OK) return st;
       stages.done("bwd_dkdv_mfma");
@@ -506,6 +507,10 @@ bsa_status_t bsa_set_tuning(bsa_tune_t key, int32_t value) {
         return fail(BSA_ERR_INVALID_ARG, "walk phase period must be 0 (off) or 1..1000000 us");
       t_walk_phase_us = value;
       return BSA_OK;
+    case BSA_TUNE_DKDV_SPLIT:
+      if (value != 0 && value != 1) return fail(BSA_ERR_INVALID_ARG, "dK/dV split must be 0 or 1");
+      t_dkdv_split = value;
+      return BSA_OK;
   }
   return fail(BSA_ERR_INVALID_ARG, "unknown tuning key");
 }
@@ -516,6 +521,7 @@ int32_t bsa_get_tuning(bsa_tune_t key) {
     case BSA_TUNE_DKDV_ORDER: return t_dkdv_order;
     case BSA_TUNE_DQ_PIPELINE: return t_dq_pipeline;
     case BSA_TUNE_WALK_PHASE: return t_walk_phase_us;
+    case BSA_TUNE_DKDV_SPLIT: return t_dkdv_split;
   }
   return INT32_MIN;
 }

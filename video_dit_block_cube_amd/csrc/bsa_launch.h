@@ -107,12 +107,13 @@ hipError_t launch_bwd_dq_pipe(const Geom& g, const bf16_t* q_row, const bf16_t* 
                               const int32_t* idx, int k_sel, float scale, float* dq,
                               int walk_ticks, hipStream_t s);
 // order: dkdv_order_bytes(g) bytes the launch fills with the longest-first item order (null:
-// the fixed XCD-balanced order).
+// the fixed XCD-balanced order).  by_keys (D = 128): the two waves of a key cube split its keys
+// (dS from the fp32 P) instead of its outputs (dS from the bf16 P handed between them).
 size_t dkdv_order_bytes(const Geom& g);
 hipError_t launch_bwd_dkdv_mfma(const Geom& g, const bf16_t* k_row, const bf16_t* v_row,
                                 const bf16_t* q_row, const bf16_t* do_row, const float2* ld_c,
                                 const int32_t* csr_off, const int32_t* csr_list, int32_t* order,
-                                float scale, int walk_ticks, float* dk, float* dv,
+                                float scale, int walk_ticks, bool by_keys, float* dk, float* dv,
                                 float* dk_cache, float* dv_cache, hipStream_t s);
 
 }  // namespace bsa

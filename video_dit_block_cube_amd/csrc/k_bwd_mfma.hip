@@ -522,6 +522,184 @@ bwd_dkdv_pair_kernel(Geom g, const bf16_t* __restrict__ k_row, const bf16_t* __r
   }
 }
 
+// ---------------------------------------------------------------------------------------------
+// dK, dV at D = 128 with two waves per key cube split by KEYS (the more accurate alternative,
+// BSA_TUNE_DKDV_SPLIT = 1): wave w holds K and V of keys 32w..32w+31 and accumulates both dK^T
+// and dV^T of those keys.  Per 16-query sub-step each wave forms S and dP of its keys (16x16x32),
+// P and dS = P o (dP - Delta) from the fp32 P (the same dS the dQ pass forms), then dV^T += dO^T P
+// and dK^T += Q^T dS (32x32x16).  No hand-off between the waves: both run the same loop and meet
+// at one barrier per 32-query step, where the step's staged rows are complete and the other
+// stage is free to be refilled (wave 0 stages the Q rows and the pairs, wave 1 the dO rows).
+// Each wave reads Q, dO, Q^T and dO^T from LDS, twice the LDS reads of the split by output,
+// which keeps this variant a few percent slower.
+// ---------------------------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) void
+bwd_dkdv_keys_kernel(Geom g, const bf16_t* __restrict__ k_row, const bf16_t* __restrict__ v_row,
+                     const bf16_t* __restrict__ q_row, const bf16_t* __restrict__ do_row,
+                     const float2* __restrict__ ld_c, const int32_t* __restrict__ csr_off,
+                     const int32_t* __restrict__ csr_list, const int32_t* __restrict__ order,
+                     float scale, float c_log2, int ccx, int ncx, int walk_ticks,
+                     float* __restrict__ dk, float* __restrict__ dv, float* __restrict__ dk_cache,
+                     float* __restrict__ dv_cache) {
+  constexpr int S4 = D / 32;
+  constexpr int DB = D / 32;
+  constexpr int cube_bytes = 64 * D * 2;
+  constexpr int half_bytes = 32 * D * 2;              // a 32-row half block in memory
+  constexpr int lds_half = staged_half_bytes<D>();    // the same block staged in LDS
+  constexpr int stage_bytes = 2 * lds_half + 256;     // Q rows | dO rows | 32 (LSE2, Delta) pairs
+  __shared__ __attribute__((aligned(16))) char stage0[stage_bytes];
+  __shared__ __attribute__((aligned(16))) char stage1[stage_bytes];
+
+  int bh, j;
+  if (order) {
+    const int it = order[blockIdx.x];
+    if (it < 0) return;
+    bh = it / g.nbk;
+    j = it % g.nbk;
+  } else if (!dkdv_identity_item(g, blockIdx.x & 7, blockIdx.x >> 3, ccx, ncx, bh, j)) {
+    return;
+  }
+  const int b = bh / g.Hh, h = bh % g.Hh;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // keys 32*wave .. +31
+  const int lane = threadIdx.x & 63;
+  const int l32 = lane & 31, hh = lane >> 5;
+
+  const int32_t* offs = csr_off + (size_t)bh * (g.nbk + 1);
+  const int beg = offs[j], end = offs[j + 1];
+  const int nsteps = 2 * (end - beg);
+  // first entry of the walk, as in the split by output
+  const int nlist = end - beg;
+  int s0 = 0;
+  if (walk_ticks > 0) {
+    __shared__ int walk_phase;
+    if (threadIdx.x == 0)
+      walk_phase = (int)((wall_clock64() % (uint64_t)walk_ticks) * (uint64_t)g.nbq /
+                         (uint64_t)walk_ticks);
+    __syncthreads();
+    const int phase = walk_phase;
+    for (int e0 = 0; e0 < nlist; e0 += 64) {
+      const int e = e0 + lane;
+      s0 += __popcll(__ballot(e < nlist && csr_list[beg + e] < phase));
+    }
+    if (s0 >= nlist) s0 = 0;
+  }
+  auto entry = [&](int e) { return csr_list[beg + (e + s0 < nlist ? e + s0 : e + s0 - nlist)]; };
+  const size_t bh_bytes = (size_t)g.nbq * cube_bytes;
+  const size_t bh_elems = (size_t)g.nbq * 64 * D;
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc((wave ? do_row : q_row) + bh * bh_elems, bh_bytes);
+  const __amdgpu_buffer_rsrc_t rl =
+      make_rsrc(ld_c + (size_t)bh * g.nbq * 64, (size_t)g.nbq * 64 * sizeof(float2));
+  lds_char* st0 = (lds_char*)stage0;
+  lds_char* st1 = (lds_char*)stage1;
+  auto stage_step = [&](int i, int qb, lds_char* dst) {
+    stage_half<D>(rs, i * cube_bytes + qb * half_bytes, dst + wave * lds_half, lane);
+    if (wave == 0)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rl, (__attribute__((address_space(3))) void*)(dst + 2 * lds_half), 4, lane * 4,
+          (i * 64 + 32 * qb) * (int)sizeof(float2), 0, 0);
+  };
+  if (nsteps > 0) stage_step(entry(0), 0, st0);
+
+  // K and V rows of this wave's 32 keys as B operands of the 16x16x32 products,
+  // f = nb*S4 + s: lane%16 = key 32*wave + 16*nb + lane%16, d = 32s + 8*(lane/16) + 0..7
+  const size_t kv_elems = (size_t)g.nbk * 64 * D;
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(k_row + bh * kv_elems, (size_t)g.nbk * cube_bytes);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(v_row + bh * kv_elems, (size_t)g.nbk * cube_bytes);
+  const int r16 = row16_lane(lane);
+  const int r16m = row16_lane_mem(lane);
+  bf16x8 kf[2 * S4], vf[2 * S4];
+#pragma unroll
+  for (int f = 0; f < 2 * S4; ++f) {
+    const int nb = f / S4, s = f % S4;
+    const int off = j * cube_bytes + wave * half_bytes + row16_const_mem<D>(s, 16 * nb);
+    kf[f] = bld16(rk, r16m, off);
+    vf[f] = bld16(rv, r16m, off);
+  }
+  f32x16 accv[DB], acck[DB];  // dV^T, dK^T of this wave's keys (lane%32 = key)
+#pragma unroll
+  for (int db = 0; db < DB; ++db) { zero16(accv[db]); zero16(acck[db]); }
+  const int trb = tr16_lane(lane);
+
+  auto step = [&](int t, lds_char* cur, lds_char* nxt) {
+    const int tn = t + 1 < nsteps ? t + 1 : t;  // the last step re-stages itself
+    __builtin_amdgcn_s_waitcnt(0x0f70);          // vmcnt(0): this wave's rows of the step landed
+    pair_barrier();  // both waves' rows have landed, and both are done with the other stage
+    stage_step(entry(tn >> 1), tn & 1, nxt);
+    const __attribute__((address_space(3))) float2* ldp =
+        (const __attribute__((address_space(3))) float2*)(cur + 2 * lds_half);
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      f32x4v sc[2], dp[2];
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        sc[nb] = f32x4v{0.f, 0.f, 0.f, 0.f};
+        dp[nb] = f32x4v{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int s = 0; s < S4; ++s) {
+        const bf16x8 a = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(
+            cur + r16 + row16_const<D>(s, 16 * sub));
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+          sc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, kf[nb * S4 + s], sc[nb], 0, 0, 0);
+      }
+#pragma unroll
+      for (int s = 0; s < S4; ++s) {
+        const bf16x8 a = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(
+            cur + lds_half + r16 + row16_const<D>(s, 16 * sub));
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+          dp[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, vf[nb * S4 + s], dp[nb], 0, 0, 0);
+      }
+      const int q0 = 16 * sub + 4 * (lane >> 4);  // this lane's first query of the sub-step
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float lx = ldp[q0 + i].x, ly = ldp[q0 + i].y;
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+          const float p = fast_exp2(fmaf(sc[nb][i], c_log2, -lx));
+          sc[nb][i] = p;
+          dp[nb][i] = p * (dp[nb][i] - ly);
+        }
+      }
+      const bf16x8 pb = acc16_to_b32(sc[0], sc[1]);
+      const bf16x8 dsb = acc16_to_b32(dp[0], dp[1]);
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+        accv[db] = mfma32(lds_tr16<D>(cur + lds_half, trb, db, sub), pb, accv[db]);
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+        acck[db] = mfma32(lds_tr16<D>(cur, trb, db, sub), dsb, acck[db]);
+    }
+  };
+  for (int t = 0; t < nsteps; t += 2) {
+    step(t, st0, st1);
+    step(t + 1, st1, st0);
+  }
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the last re-staging has landed
+
+  const bool cond = j < g.nbc;  // condition key cube: its gradients go to the cache tensors
+  const int jc = cond ? j : j - g.nbc;
+  const int tk = cube_token(g, jc, 32 * wave + l32);
+  if (tk < 0) return;  // slot outside a ragged grid
+  const size_t off = bnhd_offset(g, cond ? g.Nc : g.Nq, b, tk, h);
+  float* outk = (cond ? dk_cache : dk) + off;
+  float* outv = (cond ? dv_cache : dv) + off;
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int d = 32 * db + 8 * r4 + 4 * hh;
+      const f32x16& a = acck[db];
+      const f32x16& c = accv[db];
+      *reinterpret_cast<float4*>(outk + d) = make_float4(
+          a[4 * r4] * scale, a[4 * r4 + 1] * scale, a[4 * r4 + 2] * scale, a[4 * r4 + 3] * scale);
+      *reinterpret_cast<float4*>(outv + d) =
+          make_float4(c[4 * r4], c[4 * r4 + 1], c[4 * r4 + 2], c[4 * r4 + 3]);
+    }
+}
+
 size_t dkdv_order_bytes(const Geom& g) {
   const int ccx = (g.nbc + 7) / 8, ncx = (g.nbq + 7) / 8;
   return (size_t)g.B * g.Hh * (ccx + ncx) * 8 * sizeof(int32_t);
@@ -530,7 +708,7 @@ size_t dkdv_order_bytes(const Geom& g) {
 hipError_t launch_bwd_dkdv_mfma(const Geom& g, const bf16_t* k_row, const bf16_t* v_row,
                                 const bf16_t* q_row, const bf16_t* do_row, const float2* ld_c,
                                 const int32_t* csr_off, const int32_t* csr_list, int32_t* order,
-                                float scale, int walk_ticks, float* dk, float* dv,
+                                float scale, int walk_ticks, bool by_keys, float* dk, float* dv,
                                 float* dk_cache, float* dv_cache, hipStream_t s) {
   const int ccx = (g.nbc + 7) / 8, ncx = (g.nbq + 7) / 8;
   dim3 grid((unsigned)(g.B * g.Hh * (ccx + ncx) * 8));
@@ -547,6 +725,10 @@ hipError_t launch_bwd_dkdv_mfma(const Geom& g, const bf16_t* k_row, const bf16_t
     hipLaunchKernelGGL(bwd_dkdv_mfma_kernel<64>, grid, dim3(64), 0, s, g, k_row, v_row, q_row,
                        do_row, ld_c, csr_off, csr_list, order, scale, c_log2, ccx, ncx, dk, dv,
                        dk_cache, dv_cache);
+  else if (by_keys)
+    hipLaunchKernelGGL(bwd_dkdv_keys_kernel<128>, grid, dim3(128), 0, s, g, k_row, v_row, q_row,
+                       do_row, ld_c, csr_off, csr_list, order, scale, c_log2, ccx, ncx, walk_ticks,
+                       dk, dv, dk_cache, dv_cache);
   else
     hipLaunchKernelGGL(bwd_dkdv_pair_kernel<128>, grid, dim3(128), 0, s, g, k_row, v_row, q_row,
                        do_row, ld_c, csr_off, csr_list, order, scale, c_log2, ccx, ncx, walk_ticks,
