@@ -238,6 +238,29 @@ def bench_microbench(bsa, torch, dev, reps=3):
         flops = n_cu_simd * wps * iters * 8 * 32768.0
         res[f"mfma_bf16_{name}_{wps}wave_per_simd_tflops"] = round(
             flops / (float(np.median(ms)) * 1e-3) / 1e12, 1)
+    # independent accumulator chains per wave, per product shape, on N(0,1) operands: how much
+    # independent MFMA work a wave must keep in flight (the kernels run 2 to 8 chains)
+    chain_cfg = [(shape, ch, wps) for wps in (1, 2) for shape in (0, 1) for ch in (1, 2, 4, 8)]
+    it_c = iters // 4
+    for shape, ch, wps in chain_cfg:
+        bsa.bsa_probe_mfma_shape(ops["normal"], shape, ch, n_cu_simd * wps, it_c // 10, sinks[wps])
+    torch.cuda.synchronize()
+    ctimes = {c: [] for c in chain_cfg}
+    for _ in range(reps):
+        for shape, ch, wps in chain_cfg:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            bsa.bsa_probe_mfma_shape(ops["normal"], shape, ch, n_cu_simd * wps, it_c, sinks[wps])
+            e1.record()
+            e1.synchronize()
+            ctimes[(shape, ch, wps)].append(e0.elapsed_time(e1))
+    chains = {}
+    for (shape, ch, wps), ms in ctimes.items():
+        flops = n_cu_simd * wps * it_c * 262144.0
+        key = f"{'32x32x16' if shape == 0 else '16x16x32'}_{wps}wave_per_simd"
+        chains.setdefault(key, {})[f"chains_{ch}"] = round(
+            flops / (float(np.median(ms)) * 1e-3) / 1e12, 1)
+    res["mfma_bf16_normal_by_chains_tflops"] = chains
     tile = 32 * 1024
     buf = torch.empty(1536 * (1 << 20), dtype=torch.uint8, device=dev).view(torch.bfloat16)
     buf.view(torch.uint8).random_(0, 256, generator=gen)

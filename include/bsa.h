@@ -284,6 +284,15 @@ bsa_status_t bsa_validate_idx(const bsa_problem_t* p, const int32_t* idx, int32_
 bsa_status_t bsa_probe_mfma(const void* operands, size_t operand_bytes, int32_t waves,
                             int32_t iters, float* sink, size_t sink_bytes, hipStream_t stream);
 
+/* The same with the product shape and the chain count chosen: shape 0 = 32x32x16 (8 products of
+ * 32768 FLOP per iteration), 1 = v_mfma_f32_16x16x32_bf16 (16 products of 16384 FLOP);
+ * chains in {1, 2, 4, 8} independent accumulators per wave (1: every product depends on the one
+ * before it).  How many independent products a wave must keep in flight for the full rate.
+ * Errors: INVALID_ARG (bad shape or chains, as above), HIP. */
+bsa_status_t bsa_probe_mfma_shape(const void* operands, size_t operand_bytes, int32_t shape,
+                                  int32_t chains, int32_t waves, int32_t iters, float* sink,
+                                  size_t sink_bytes, hipStream_t stream);
+
 /* Whole-tile reads: wave w (workgroup w, which runs on XCD w % 8) reads tiles
  * ids[w * tiles_per_wave + t] of `buf` (tile_bytes each, a multiple of 8192 up to 1 MiB) as
  * 1 KB wave-wide 16-byte-per-lane loads -- the attention kernels' tile access pattern.  Ids

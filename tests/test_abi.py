@@ -220,3 +220,12 @@ def test_validate_idx_rejects_bad_arguments_on_host(L):
     assert L.bsa_validate_idx(ctypes.byref(p), FAKE, 0, bad, None) == INVALID   # k_sel < 1
     assert L.bsa_validate_idx(ctypes.byref(p), FAKE, 9, bad, None) == INVALID   # k_sel > nbk
     assert L.bsa_validate_idx(ctypes.byref(_p(head_dim=96)), FAKE, 1, bad, None) == UNSUPPORTED
+
+
+def test_probe_arguments_are_checked_on_host(L):
+    fake = ctypes.c_void_p(0x10000)
+    for shape, chains in ((2, 4), (-1, 4), (0, 3), (1, 16), (0, 0)):
+        assert L.bsa_probe_mfma_shape(fake, 8192, shape, chains, 1, 1, fake, 256, None) == INVALID
+    assert L.bsa_probe_mfma_shape(None, 8192, 0, 4, 1, 1, fake, 256, None) == INVALID
+    assert L.bsa_probe_mfma_shape(fake, 4096, 0, 4, 1, 1, fake, 256, None) == INVALID
+    assert L.bsa_probe_mfma_shape(fake, 8192, 0, 4, 2, 1, fake, 256, None) == INVALID  # sink

@@ -119,6 +119,7 @@ def lib() -> ctypes.CDLL:
             "bsa_sparse_attn_fwd_noalloc": (i32, [P, i32, vp, vp, vp, vp, vp, vp, i32, f32, vp,
                                                   vp, vp]),
             "bsa_probe_mfma": (i32, [vp, sz, i32, i32, vp, sz, vp]),
+            "bsa_probe_mfma_shape": (i32, [vp, sz, i32, i32, i32, i32, vp, sz, vp]),
             "bsa_probe_tile_read": (i32, [vp, sz, i32, vp, sz, i32, i32, vp, sz, vp]),
         }
         for name, (res, args) in sigs.items():
@@ -430,6 +431,16 @@ def bsa_probe_mfma(operands: torch.Tensor, waves: int, iters: int, sink: torch.T
     _check(lib().bsa_probe_mfma(_ptr(operands, "operands"), operands.numel() * operands.element_size(),
                                 int(waves), int(iters), _ptr(sink, "sink"),
                                 sink.numel() * sink.element_size(), _stream(operands)))
+
+
+def bsa_probe_mfma_shape(operands: torch.Tensor, shape: int, chains: int, waves: int, iters: int,
+                         sink: torch.Tensor) -> None:
+    """Back-to-back bf16 MFMA of one shape (0: 32x32x16, 1: 16x16x32) with `chains` independent
+    accumulators per wave, iters x 262144 FLOP per wave."""
+    _check(lib().bsa_probe_mfma_shape(_ptr(operands, "operands"),
+                                      operands.numel() * operands.element_size(), int(shape),
+                                      int(chains), int(waves), int(iters), _ptr(sink, "sink"),
+                                      sink.numel() * sink.element_size(), _stream(operands)))
 
 
 def bsa_probe_tile_read(buf: torch.Tensor, tile_bytes: int, ids: torch.Tensor,

@@ -526,22 +526,33 @@ int32_t bsa_get_tuning(bsa_tune_t key) {
   return INT32_MIN;
 }
 
-bsa_status_t bsa_probe_mfma(const void* operands, size_t operand_bytes, int32_t waves,
-                            int32_t iters, float* sink, size_t sink_bytes, hipStream_t stream) {
+bsa_status_t bsa_probe_mfma_shape(const void* operands, size_t operand_bytes, int32_t shape,
+                                  int32_t chains, int32_t waves, int32_t iters, float* sink,
+                                  size_t sink_bytes, hipStream_t stream) {
   return guarded([&]() -> bsa_status_t {
     if (!operands || !sink) return fail(BSA_ERR_INVALID_ARG, "operands and sink must be non-NULL");
     if (operand_bytes < 8192) return fail(BSA_ERR_INVALID_ARG, "operands must hold 8192 bytes");
+    if (shape != 0 && shape != 1) return fail(BSA_ERR_INVALID_ARG, "shape must be 0 or 1");
+    if (chains != 1 && chains != 2 && chains != 4 && chains != 8)
+      return fail(BSA_ERR_INVALID_ARG, "chains must be 1, 2, 4 or 8");
     if (waves < 1 || waves > (1 << 22) || iters < 1)
       return fail(BSA_ERR_INVALID_ARG, "waves must be in 1..2^22 and iters >= 1");
     if (sink_bytes < (size_t)waves * 64 * sizeof(float))
       return fail(BSA_ERR_INVALID_ARG, "sink must hold 64 floats per wave");
     Stages stages(stream);
-    const bsa_status_t st = hip_status(
-        launch_mfma_probe(static_cast<const bf16_t*>(operands), waves, iters, sink, stream),
-        "MFMA probe launch");
+    const bsa_status_t st = hip_status(launch_mfma_probe(static_cast<const bf16_t*>(operands),
+                                                         shape, chains, waves, iters, sink,
+                                                         stream),
+                                       "MFMA probe launch");
     stages.done("probe_mfma");
     return st;
   });
+}
+
+bsa_status_t bsa_probe_mfma(const void* operands, size_t operand_bytes, int32_t waves,
+                            int32_t iters, float* sink, size_t sink_bytes, hipStream_t stream) {
+  return bsa_probe_mfma_shape(operands, operand_bytes, 0, 4, waves, iters, sink, sink_bytes,
+                              stream);
 }
 
 bsa_status_t bsa_probe_tile_read(const void* buf, size_t buf_bytes, int32_t tile_bytes,

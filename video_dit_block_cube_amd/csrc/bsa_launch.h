@@ -58,8 +58,8 @@ hipError_t launch_validate_idx(const Geom& g, const int32_t* idx, int k_sel, int
 // k_probe.hip (diagnostics): back-to-back bf16 MFMA on `waves` one-wave workgroups (operands:
 // 8 x 1 KB of bf16 at `operands`; sink: 64 floats per wave), and whole-tile reads of the tiles
 // listed in ids ([waves, tiles_per_wave] tile numbers of buf; sink: 64 words per wave).
-hipError_t launch_mfma_probe(const bf16_t* operands, int waves, int iters, float* sink,
-                             hipStream_t s);
+hipError_t launch_mfma_probe(const bf16_t* operands, int shape, int chains, int waves, int iters,
+                             float* sink, hipStream_t s);
 hipError_t launch_tile_read(const bf16_t* buf, size_t buf_bytes, int tile_bytes,
                             const int32_t* ids, int waves, int tiles_per_wave, uint32_t* sink,
                             hipStream_t s);

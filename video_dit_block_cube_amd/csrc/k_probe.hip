@@ -1,8 +1,8 @@
 // k_probe.hip -- two microbenchmarks that bound the attention kernels on MI355X (diagnostics; no
 // part of block sparse attention runs here):
 //
-//  * mfma_probe_kernel: back-to-back v_mfma_f32_32x32x16_bf16 on every SIMD, four independent
-//    accumulator chains per wave, operands taken from a caller buffer.  With N(0,1) bf16 operands
+//  * mfma_probe_kernel: back-to-back v_mfma_f32_32x32x16_bf16 (or 16x16x32) on every SIMD, with
+//    1, 2, 4 or 8 independent accumulator chains per wave, operands taken from a caller buffer.  With N(0,1) bf16 operands
 //    (the data the attention products see) the chip lowers its clock under load, so this is the
 //    rate bf16 MFMA work can reach on such data; constant operands show the clock effect.
 //  * tile_read_kernel: every wave reads whole tiles (tile_bytes, a multiple of 1 KB) at the tile
@@ -21,6 +21,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t probe_rsrc(const void* base, s
 }
 }  // namespace
 
+// SHAPE 0: v_mfma_f32_32x32x16_bf16, 8 products per iteration; SHAPE 1: v_mfma_f32_16x16x32_bf16,
+// 16 products per iteration (262144 FLOP per iteration either way).  CH independent accumulator
+// chains per wave, product u adding into chain u % CH: one chain makes every product depend on
+// the one before it.
+template <int SHAPE, int CH>
 __global__ __launch_bounds__(64) void mfma_probe_kernel(const bf16_t* __restrict__ operands,
                                                         int iters, float* __restrict__ sink) {
   const int lane = threadIdx.x;
@@ -29,22 +34,41 @@ __global__ __launch_bounds__(64) void mfma_probe_kernel(const bf16_t* __restrict
   for (int u = 0; u < 8; ++u)
     a[u] = __builtin_bit_cast(bf16x8,
                               *reinterpret_cast<const uint4*>(operands + (u * 64 + lane) * 8));
-  f32x16 acc[4];
-#pragma unroll
-  for (int c = 0; c < 4; ++c)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) acc[c][e] = 0.f;
-  for (int it = 0; it < iters; ++it) {
-#pragma unroll
-    for (int u = 0; u < 8; ++u)
-      acc[u & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[u], a[(u + 3) & 7], acc[u & 3], 0,
-                                                           0, 0);
-  }
   float s = 0.f;
+  if constexpr (SHAPE == 0) {
+    f32x16 acc[CH];
 #pragma unroll
-  for (int c = 0; c < 4; ++c)
+    for (int c = 0; c < CH; ++c)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) s += acc[c][e];
+      for (int e = 0; e < 16; ++e) acc[c][e] = 0.f;
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        acc[u % CH] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[u], a[(u + 3) & 7], acc[u % CH],
+                                                              0, 0, 0);
+    }
+#pragma unroll
+    for (int c = 0; c < CH; ++c)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) s += acc[c][e];
+  } else {
+    typedef float f32x4p __attribute__((ext_vector_type(4)));
+    f32x4p acc[CH];
+#pragma unroll
+    for (int c = 0; c < CH; ++c)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[c][e] = 0.f;
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+      for (int u = 0; u < 16; ++u)
+        acc[u % CH] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u & 7], a[(u + 3) & 7],
+                                                              acc[u % CH], 0, 0, 0);
+    }
+#pragma unroll
+    for (int c = 0; c < CH; ++c)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s += acc[c][e];
+  }
   sink[blockIdx.x * 64 + lane] = s;
 }
 
@@ -76,10 +100,23 @@ __global__ __launch_bounds__(64) void tile_read_kernel(const bf16_t* __restrict_
   sink[blockIdx.x * 64 + lane] = x;
 }
 
-hipError_t launch_mfma_probe(const bf16_t* operands, int waves, int iters, float* sink,
-                             hipStream_t s) {
-  hipLaunchKernelGGL(mfma_probe_kernel, dim3((unsigned)waves), dim3(64), 0, s, operands, iters,
-                     sink);
+hipError_t launch_mfma_probe(const bf16_t* operands, int shape, int chains, int waves, int iters,
+                             float* sink, hipStream_t s) {
+  const dim3 grid((unsigned)waves), block(64);
+#define BSA_PROBE(SH, CH) \
+  hipLaunchKernelGGL((mfma_probe_kernel<SH, CH>), grid, block, 0, s, operands, iters, sink)
+  switch (shape * 16 + chains) {
+    case 1: BSA_PROBE(0, 1); break;
+    case 2: BSA_PROBE(0, 2); break;
+    case 4: BSA_PROBE(0, 4); break;
+    case 8: BSA_PROBE(0, 8); break;
+    case 17: BSA_PROBE(1, 1); break;
+    case 18: BSA_PROBE(1, 2); break;
+    case 20: BSA_PROBE(1, 4); break;
+    case 24: BSA_PROBE(1, 8); break;
+    default: return hipErrorInvalidValue;
+  }
+#undef BSA_PROBE
   return hipGetLastError();
 }
 
