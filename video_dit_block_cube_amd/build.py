@@ -27,11 +27,23 @@ FLAGS = [
     "-I", INCLUDE, "-I", CSRC,
 ]
 
-# Per-file flags.  The dQ backward keeps its score accumulators and the dQ^T accumulators apart
-# under LLVM's register-minimising scheduler, which removes AGPR<->VGPR copies from its loop
-# (about 2-3% faster at the 720p-class shape); the other kernels are best with the default.
+# Per-file flags (LLVM AMDGPU options; every choice measured at the 720p-class shape, same bits):
+#  * MINREG, LLVM's register-minimising scheduler: the head_dim 128 one-wave dQ then keeps its
+#    score accumulators out of the AGPRs that hold dQ^T (about 2-3% faster).
+#  * VGPR_MFMA, every MFMA writing architectural VGPRs.  Without it the compiler gives every MFMA
+#    an AGPR destination once a kernel may use more than 256 registers, and each score element
+#    then costs a v_accvgpr_read before its exponential.  The pipelined dQ (512 registers) loses
+#    its 128 copies per tile with it (with MINREG: no spills; 2.5% faster); the head_dim 64 dQ
+#    and dK/dV fit in 256 VGPRs with it (8% faster each).  The head_dim 128 dK/dV kernels already
+#    use VGPRs only and compile to the same code; the head_dim 128 one-wave dQ was 2% slower with
+#    it, so k_bwd_dq.hip does without.
+MINREG = ["-mllvm", "--amdgpu-sched-strategy=iterative-minreg"]
+VGPR_MFMA = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
 EXTRA_FLAGS = {
-    "k_bwd_dq.hip": ["-mllvm", "--amdgpu-sched-strategy=iterative-minreg"],
+    "k_bwd_dq.hip": MINREG,
+    "k_bwd_dq64.hip": VGPR_MFMA,
+    "k_bwd_dq_pipe.hip": VGPR_MFMA + MINREG,
+    "k_bwd_mfma.hip": VGPR_MFMA,
 }
 
 

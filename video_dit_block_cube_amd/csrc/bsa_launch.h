@@ -102,6 +102,12 @@ hipError_t launch_bwd_dq_mfma(const Geom& g, const bf16_t* q_row, const bf16_t* 
                               const bf16_t* k_row, const bf16_t* v_row, const float2* ld_c,
                               const int32_t* idx, int k_sel, float scale, float* dq,
                               bool pipelined, int walk_ticks, hipStream_t s);
+// k_bwd_dq64.hip: the one-wave dQ kernel at head_dim 64 (grid B*Hh*cpx*8 waves, cpx = query
+// cubes per XCD slice); called by launch_bwd_dq_mfma.
+hipError_t launch_bwd_dq64(const Geom& g, const bf16_t* q_row, const bf16_t* do_row,
+                           const bf16_t* k_row, const bf16_t* v_row, const float2* ld_c,
+                           const int32_t* idx, int k_sel, float scale, float c_log2, int cpx,
+                           float* dq, hipStream_t s);
 hipError_t launch_bwd_dq_pipe(const Geom& g, const bf16_t* q_row, const bf16_t* do_row,
                               const bf16_t* k_row, const bf16_t* v_row, const float2* ld_c,
                               const int32_t* idx, int k_sel, float scale, float* dq,

@@ -9,12 +9,15 @@
 // MI355X design: one wave per query cube, as in the plain dQ kernel, but the tile loop is
 // software-pipelined by one tile.  S^T and dP^T of tile t+1 go to the MFMA unit while the VALU
 // forms P and dS of tile t, then dQ^T takes tile t's product.  At head_dim 128 the dQ^T
-// accumulators, the score accumulators of two tiles and the Q/dO operands need 512 registers, so
+// accumulators, the score accumulators of two tiles and the Q/dO operands need 486 registers, so
 // one wave runs per SIMD and no other wave can fill the MFMA unit during the exponentials.  Each
 // tile's arithmetic and the order of the dQ^T updates are those of the plain loop, so the result
-// is the same bit for bit.  Built with LLVM's default scheduler (6% faster than the plain kernel
-// at the 720p-class shape; the same pipelining at head_dim 64 or with the ragged-grid clamp was
-// slower than the plain kernel there, so those keep it).
+// is the same bit for bit.  Built with every MFMA writing architectural VGPRs and LLVM's
+// register-minimising scheduler (build flags): the accumulators then sit in VGPRs, where the
+// exponentials read the scores without a copy per element, and the Q and dO operand fragments,
+// which the products read straight from there, fill the AGPRs.  About 8% faster than the plain kernel at the 720p-class shape; the same pipelining at
+// head_dim 64 or with the ragged-grid clamp was slower than the plain kernel there, so those keep
+// it.
 #include "bsa_bwd_tiles.h"
 
 namespace bsa {

@@ -26,8 +26,8 @@ namespace bsa {
 // S = Q K^T and dP = dO V^T take them as A operands against the key cube's K and V rows held in
 // registers, and P, dS are the B operands of dV^T += dO^T P and dK^T += Q^T dS, whose A operands
 // are read transposed from the same staged rows.  Two kernels:
-//   bwd_dkdv_mfma_kernel (D = 64): one wave per key cube, 16-query sub-steps (248 registers,
-//     two waves per SIMD);
+//   bwd_dkdv_mfma_kernel (D = 64): one wave per key cube, 16-query sub-steps (254 VGPRs, every
+//     MFMA writing VGPRs by the build flags, so no AGPR copies; two waves per SIMD);
 //   bwd_dkdv_pair_kernel (D = 128): two waves per key cube split by output (below).
 // ---------------------------------------------------------------------------------------------
 // XCD x takes the x-th run of ccx condition cube ids and the x-th run of ncx noise cube ids of
