@@ -191,11 +191,18 @@ __global__ __launch_bounds__(64) void bwd_dkdv_mfma_kernel(
     // two 16-query sub-steps per staged half
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
+      // (base-2 LSE, Delta) of this lane's queries 16*sub + 4*(lane/16) + 0..3
+      const f32x4 p01 = ldp[8 * sub + 2 * (lane >> 4)];
+      const f32x4 p23 = ldp[8 * sub + 2 * (lane >> 4) + 1];
+      const float lv[4] = {p01[0], p01[2], p23[0], p23[2]};
+      // dP's accumulators start at -Delta of the lane's queries, so the products leave the
+      // factor dP - Delta of dS with no subtraction per element
+      const f32x4v ndl = f32x4v{-p01[1], -p01[3], -p23[1], -p23[3]};
       f32x4v sc[4], dp[4];
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb) {
         sc[nb] = f32x4v{0.f, 0.f, 0.f, 0.f};
-        dp[nb] = sc[nb];
+        dp[nb] = ndl;
       }
 #pragma unroll
       for (int s = 0; s < S4; ++s) {
@@ -205,11 +212,6 @@ __global__ __launch_bounds__(64) void bwd_dkdv_mfma_kernel(
         for (int nb = 0; nb < 4; ++nb)
           sc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, kreg[nb * S4 + s], sc[nb], 0, 0, 0);
       }
-      // (base-2 LSE, Delta) of this lane's queries 16*sub + 4*(lane/16) + 0..3
-      const f32x4 p01 = ldp[8 * sub + 2 * (lane >> 4)];
-      const f32x4 p23 = ldp[8 * sub + 2 * (lane >> 4) + 1];
-      const float lv[4] = {p01[0], p01[2], p23[0], p23[2]};
-      const float dl[4] = {p01[1], p01[3], p23[1], p23[3]};
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
@@ -228,7 +230,7 @@ __global__ __launch_bounds__(64) void bwd_dkdv_mfma_kernel(
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dp[nb][i] = sc[nb][i] * (dp[nb][i] - dl[i]);
+        for (int i = 0; i < 4; ++i) dp[nb][i] = sc[nb][i] * dp[nb][i];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) dsb[kb] = acc16_to_b32(dp[2 * kb], dp[2 * kb + 1]);
 #pragma unroll
@@ -400,9 +402,18 @@ bwd_dkdv_pair_kernel(Geom g, const bf16_t* __restrict__ k_row, const bf16_t* __r
         (const __attribute__((address_space(3))) float2*)(cur + own_pairs);
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
+      const int q0 = 16 * sub + 4 * (lane >> 4);  // this lane's first query of the sub-step
+      // Score accumulators start at 0 for S (wave 0) and at -Delta of the lane's four queries
+      // for dP (wave 1), so the products leave dP - Delta, the factor dS needs, with no
+      // subtraction per element (the four values serve all four key blocks).
       f32x4v sc[4];
+      f32x4v c0 = f32x4v{0.f, 0.f, 0.f, 0.f};
+      if constexpr (R == 1) {
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) sc[nb] = f32x4v{0.f, 0.f, 0.f, 0.f};
+        for (int i = 0; i < 4; ++i) c0[i] = -ldp[q0 + i].y;
+      }
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) sc[nb] = c0;
       // Operand reads are issued ahead of their products, so the LDS latency overlaps other
       // work: the wave's own row fragments of the sub-step first, and the transposed fragments
       // of the other wave's rows (dO^T for wave 0, Q^T for wave 1) as soon as they are visible:
@@ -430,7 +441,6 @@ bwd_dkdv_pair_kernel(Geom g, const bf16_t* __restrict__ k_row, const bf16_t* __r
       typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
       __attribute__((address_space(3))) u32x4* x =
           (__attribute__((address_space(3))) u32x4*)(xch[sub]) + lane;
-      const int q0 = 16 * sub + 4 * (lane >> 4);  // this lane's first query of the sub-step
       if constexpr (R == 0) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -466,7 +476,8 @@ bwd_dkdv_pair_kernel(Geom g, const bf16_t* __restrict__ k_row, const bf16_t* __r
         const u32x4 xa = x[0], xb = x[64];
         __builtin_amdgcn_sched_barrier(0);
         if (sub == 0) stage_step(entry(tn >> 1), tn & 1, nxt);
-        // dS = P o (dP - Delta) from wave 0's bf16 P (same lane layout as this accumulator)
+        // dS = P o (dP - Delta) from wave 0's bf16 P (same lane layout as this accumulator,
+        // which already holds dP - Delta)
         const uint32_t xw[8] = {xa[0], xa[1], xa[2], xa[3], xb[0], xb[1], xb[2], xb[3]};
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb) {
@@ -474,7 +485,7 @@ bwd_dkdv_pair_kernel(Geom g, const bf16_t* __restrict__ k_row, const bf16_t* __r
           const float pv[4] = {__uint_as_float(w0 << 16), __uint_as_float(w0 & 0xffff0000u),
                                __uint_as_float(w1 << 16), __uint_as_float(w1 & 0xffff0000u)};
 #pragma unroll
-          for (int i = 0; i < 4; ++i) sc[nb][i] = pv[i] * (sc[nb][i] - ldp[q0 + i].y);
+          for (int i = 0; i < 4; ++i) sc[nb][i] = pv[i] * sc[nb][i];
         }
         bf16x8 dsb[2];
 #pragma unroll
@@ -630,11 +641,17 @@ bwd_dkdv_keys_kernel(Geom g, const bf16_t* __restrict__ k_row, const bf16_t* __r
         (const __attribute__((address_space(3))) float2*)(cur + 2 * lds_half);
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
+      const int q0 = 16 * sub + 4 * (lane >> 4);  // this lane's first query of the sub-step
+      // dP's accumulators start at -Delta of the lane's four queries (dP - Delta comes out of
+      // the products)
+      f32x4v ndl;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ndl[i] = -ldp[q0 + i].y;
       f32x4v sc[2], dp[2];
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
         sc[nb] = f32x4v{0.f, 0.f, 0.f, 0.f};
-        dp[nb] = f32x4v{0.f, 0.f, 0.f, 0.f};
+        dp[nb] = ndl;
       }
 #pragma unroll
       for (int s = 0; s < S4; ++s) {
@@ -652,15 +669,14 @@ bwd_dkdv_keys_kernel(Geom g, const bf16_t* __restrict__ k_row, const bf16_t* __r
         for (int nb = 0; nb < 2; ++nb)
           dp[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, vf[nb * S4 + s], dp[nb], 0, 0, 0);
       }
-      const int q0 = 16 * sub + 4 * (lane >> 4);  // this lane's first query of the sub-step
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float lx = ldp[q0 + i].x, ly = ldp[q0 + i].y;
+        const float lx = ldp[q0 + i].x;
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) {
           const float p = fast_exp2(fmaf(sc[nb][i], c_log2, -lx));
           sc[nb][i] = p;
-          dp[nb][i] = p * (dp[nb][i] - ly);
+          dp[nb][i] = p * dp[nb][i];
         }
       }
       const bf16x8 pb = acc16_to_b32(sc[0], sc[1]);
