@@ -207,10 +207,12 @@ def cpu_baseline(x, op, r):
 
 
 def bench_microbench(bsa, torch, dev, reps=3):
-    """The two limits the attention kernels run against, measured with the library's probe
-    kernels: back-to-back bf16 MFMA on N(0,1) against constant operands at one and two waves per
-    SIMD, and whole 32 KB tile reads at the working sets the kernels see per XCD (a forward key
-    range, half of one, one head's K/V shared by every XCD, the whole 1.5 GB of K/V)."""
+    """The limits the attention kernels run against, measured with the library's probe kernels:
+    back-to-back bf16 MFMA on N(0,1) against constant operands at one and two waves per SIMD and
+    by product shape and accumulator chains; MFMA beside VALU work, within a wave and across the
+    two waves of a SIMD; and whole 32 KB tile reads at the working sets the kernels see per XCD
+    (a forward key range, half of one, one head's K/V shared by every XCD, the whole 1.5 GB of
+    K/V)."""
     import numpy as np
     res = {}
     gen = torch.Generator(device=dev)
@@ -261,6 +263,37 @@ def bench_microbench(bsa, torch, dev, reps=3):
         chains.setdefault(key, {})[f"chains_{ch}"] = round(
             flops / (float(np.median(ms)) * 1e-3) / 1e12, 1)
     res["mfma_bf16_normal_by_chains_tflops"] = chains
+    # bf16 MFMA beside VALU work on one SIMD: interleaved in every wave (mode 0), split between
+    # the two waves of a SIMD (mode 1), against products only (2) and VALU only (3).  "overlap" =
+    # the share of the shorter kind's time hidden under the other: 1 = fully beside, 0 = after.
+    wgs, it_x = 1024, 8000
+    xsink = torch.empty(wgs * 512, dtype=torch.float32, device=dev)
+    xcfg = [(op, v, acc) for acc in (0, 1) for op, vs in ((0, (4, 8, 16)), (1, (2, 4)))
+            for v in vs]
+    for op, v, acc in xcfg:
+        for mode in range(4):
+            bsa.bsa_probe_mfma_valu(ops["normal"], mode, v, op, acc, wgs, it_x // 10, xsink)
+    torch.cuda.synchronize()
+    xt = {(op, v, acc, m): [] for op, v, acc in xcfg for m in range(4)}
+    for _ in range(reps):
+        for op, v, acc in xcfg:
+            for mode in range(4):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                bsa.bsa_probe_mfma_valu(ops["normal"], mode, v, op, acc, wgs, it_x, xsink)
+                e1.record()
+                e1.synchronize()
+                xt[(op, v, acc, mode)].append(e0.elapsed_time(e1))
+    coexec = {}
+    for op, v, acc in xcfg:
+        t = [float(np.median(xt[(op, v, acc, m)])) for m in range(4)]
+        both, half = t[2] + t[3], 0.5 * (t[2] + t[3])
+        coexec[f"{'fma' if op == 0 else 'exp'}_x{v}_per_mfma_{'agpr' if acc else 'vgpr'}_acc"] = {
+            "mfma_only_ms": round(t[2], 3), "valu_only_ms": round(t[3], 3),
+            "in_wave_ms": round(t[0], 3), "across_waves_ms": round(t[1], 3),
+            "overlap_in_wave": round((both - t[0]) / min(t[2], t[3]), 2),
+            "overlap_across_waves": round((half - t[1]) / (0.5 * min(t[2], t[3])), 2)}
+    res["mfma_valu_coexec"] = coexec
     tile = 32 * 1024
     buf = torch.empty(1536 * (1 << 20), dtype=torch.uint8, device=dev).view(torch.bfloat16)
     buf.view(torch.uint8).random_(0, 256, generator=gen)
@@ -289,8 +322,9 @@ def bench_microbench(bsa, torch, dev, reps=3):
         res[f"tile_read_{name}_TBps"] = round(waves * per_wave * tile /
                                               (float(np.median(ms)) * 1e-3) / 1e12, 2)
     del buf
-    res["note"] = ("MFMA: 8 products x iters per wave on 1024 or 2048 one-wave workgroups; tile "
-                   "reads: 2048 waves x 64 random 32 KB tiles, 1 KB wave loads")
+    res["note"] = ("MFMA: 8 products x iters per wave on 1024 or 2048 one-wave workgroups; "
+                   "MFMA beside VALU: 1024 eight-wave workgroups (one per CU at a time) x 8000 x 4 "
+                   "products; tile reads: 2048 waves x 64 random 32 KB tiles, 1 KB wave loads")
     return res
 
 
@@ -317,7 +351,7 @@ def main() -> int:
     ap.add_argument("--no-microbench", action="store_true",
                     help="skip the MFMA-rate and tile-read microbenchmarks")
     ap.add_argument("--only-leg", choices=["480p", "continuation", "ragged", "d64", "smooth",
-                                           "walk", "dkdv_split"],
+                                           "walk", "dkdv_split", "microbench"],
                     help="run only this extra measurement (no headline step), e.g. to profile it")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
@@ -342,7 +376,8 @@ def main() -> int:
                 "ragged": lambda: bench_ragged(bsa, synth, torch, dev, args),
                 "smooth": lambda: bench_smooth(bsa, synth, torch, dev),
                 "walk": lambda: bench_walk(bsa, synth, torch, dev),
-                "dkdv_split": lambda: bench_dkdv_split(bsa, synth, torch, dev)}
+                "dkdv_split": lambda: bench_dkdv_split(bsa, synth, torch, dev),
+                "microbench": lambda: bench_microbench(bsa, torch, dev)}
         log(f"only the {args.only_leg} measurement")
         print(json.dumps({"leg": args.only_leg, "result": legs[args.only_leg]()}), flush=True)
         return 0

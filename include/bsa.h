@@ -293,6 +293,23 @@ bsa_status_t bsa_probe_mfma_shape(const void* operands, size_t operand_bytes, in
                                   int32_t chains, int32_t waves, int32_t iters, float* sink,
                                   size_t sink_bytes, hipStream_t stream);
 
+/* bf16 MFMA beside VALU work on one SIMD: `workgroups` eight-wave workgroups (two waves on every
+ * SIMD of a CU), each wave iterating `iters` times over four v_mfma_f32_32x32x16_bf16 products
+ * (four independent accumulators, operands from the first 2048 bytes of `operands`), each
+ * product followed by `valu` VALU instructions on eight independent fp32 chains (op 0:
+ * v_fma_f32; op 1: v_exp_f32).  mode 0: every wave does both, the VALU instructions scheduled
+ * right after each product; 1: of the two waves on a SIMD one does the products and the other
+ * the VALU instructions; 2: products only; 3: VALU instructions only.  Comparing the modes
+ * shows how much VALU work (the softmax of the attention kernels) can run beside the products
+ * within a wave and across the waves of a SIMD.  valu: {0, 2, 4, 8, 16} for op 0, {1, 2, 4} for
+ * op 1.  acc 0: the products accumulate in VGPRs (what the compiler picks for a kernel within
+ * 256 registers); 1: in AGPRs.  sink: device, >= 512 floats per workgroup, overwritten.
+ * Errors: INVALID_ARG, HIP. */
+bsa_status_t bsa_probe_mfma_valu(const void* operands, size_t operand_bytes, int32_t mode,
+                                 int32_t valu, int32_t op, int32_t acc, int32_t workgroups,
+                                 int32_t iters, float* sink, size_t sink_bytes,
+                                 hipStream_t stream);
+
 /* Whole-tile reads: wave w (workgroup w, which runs on XCD w % 8) reads tiles
  * ids[w * tiles_per_wave + t] of `buf` (tile_bytes each, a multiple of 8192 up to 1 MiB) as
  * 1 KB wave-wide 16-byte-per-lane loads -- the attention kernels' tile access pattern.  Ids

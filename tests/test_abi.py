@@ -229,3 +229,11 @@ def test_probe_arguments_are_checked_on_host(L):
     assert L.bsa_probe_mfma_shape(None, 8192, 0, 4, 1, 1, fake, 256, None) == INVALID
     assert L.bsa_probe_mfma_shape(fake, 4096, 0, 4, 1, 1, fake, 256, None) == INVALID
     assert L.bsa_probe_mfma_shape(fake, 8192, 0, 4, 2, 1, fake, 256, None) == INVALID  # sink
+    for mode, valu, op, acc in ((4, 4, 0, 0), (-1, 4, 0, 0), (0, 3, 0, 0), (0, 32, 0, 0),
+                                (0, 8, 1, 0), (0, 0, 1, 0), (0, 4, 2, 0), (0, 4, 0, 2)):
+        assert L.bsa_probe_mfma_valu(fake, 2048, mode, valu, op, acc, 1, 1, fake, 2048,
+                                     None) == INVALID
+    assert L.bsa_probe_mfma_valu(None, 2048, 0, 4, 0, 0, 1, 1, fake, 2048, None) == INVALID
+    assert L.bsa_probe_mfma_valu(fake, 1024, 0, 4, 0, 0, 1, 1, fake, 2048, None) == INVALID
+    assert L.bsa_probe_mfma_valu(fake, 2048, 0, 4, 0, 0, 2, 1, fake, 2048, None) == INVALID
+    assert L.bsa_probe_mfma_valu(fake, 2048, 0, 4, 0, 0, 0, 1, fake, 2048, None) == INVALID

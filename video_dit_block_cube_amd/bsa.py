@@ -120,6 +120,7 @@ def lib() -> ctypes.CDLL:
                                                   vp, vp]),
             "bsa_probe_mfma": (i32, [vp, sz, i32, i32, vp, sz, vp]),
             "bsa_probe_mfma_shape": (i32, [vp, sz, i32, i32, i32, i32, vp, sz, vp]),
+            "bsa_probe_mfma_valu": (i32, [vp, sz, i32, i32, i32, i32, i32, i32, vp, sz, vp]),
             "bsa_probe_tile_read": (i32, [vp, sz, i32, vp, sz, i32, i32, vp, sz, vp]),
         }
         for name, (res, args) in sigs.items():
@@ -441,6 +442,19 @@ def bsa_probe_mfma_shape(operands: torch.Tensor, shape: int, chains: int, waves:
                                       operands.numel() * operands.element_size(), int(shape),
                                       int(chains), int(waves), int(iters), _ptr(sink, "sink"),
                                       sink.numel() * sink.element_size(), _stream(operands)))
+
+
+def bsa_probe_mfma_valu(operands: torch.Tensor, mode: int, valu: int, op: int, acc: int,
+                        workgroups: int, iters: int, sink: torch.Tensor) -> None:
+    """bf16 MFMA beside VALU work on one SIMD (mode 0: interleaved in every wave; 1: split between
+    the two waves of a SIMD; 2: products only; 3: VALU only), iters x 4 products per wave, each
+    followed by `valu` VALU instructions (op 0: fma, 1: exp); accumulators in VGPRs (acc 0) or
+    AGPRs (acc 1)."""
+    _check(lib().bsa_probe_mfma_valu(_ptr(operands, "operands"),
+                                     operands.numel() * operands.element_size(), int(mode),
+                                     int(valu), int(op), int(acc), int(workgroups), int(iters),
+                                     _ptr(sink, "sink"), sink.numel() * sink.element_size(),
+                                     _stream(operands)))
 
 
 def bsa_probe_tile_read(buf: torch.Tensor, tile_bytes: int, ids: torch.Tensor,

@@ -555,6 +555,32 @@ bsa_status_t bsa_probe_mfma(const void* operands, size_t operand_bytes, int32_t 
                               stream);
 }
 
+bsa_status_t bsa_probe_mfma_valu(const void* operands, size_t operand_bytes, int32_t mode,
+                                 int32_t valu, int32_t op, int32_t acc, int32_t workgroups,
+                                 int32_t iters, float* sink, size_t sink_bytes,
+                                 hipStream_t stream) {
+  return guarded([&]() -> bsa_status_t {
+    if (!operands || !sink) return fail(BSA_ERR_INVALID_ARG, "operands and sink must be non-NULL");
+    if (operand_bytes < 2048) return fail(BSA_ERR_INVALID_ARG, "operands must hold 2048 bytes");
+    if (mode < 0 || mode > 3) return fail(BSA_ERR_INVALID_ARG, "mode must be 0, 1, 2 or 3");
+    const bool ok = op == 0 ? (valu == 0 || valu == 2 || valu == 4 || valu == 8 || valu == 16)
+                            : op == 1 && (valu == 1 || valu == 2 || valu == 4);
+    if (!ok) return fail(BSA_ERR_INVALID_ARG, "valu must be 0, 2, 4, 8 or 16 (op 0), 1, 2 or 4 (op 1)");
+    if (acc != 0 && acc != 1) return fail(BSA_ERR_INVALID_ARG, "acc must be 0 or 1");
+    if (workgroups < 1 || workgroups > (1 << 20) || iters < 1)
+      return fail(BSA_ERR_INVALID_ARG, "workgroups must be in 1..2^20 and iters >= 1");
+    if (sink_bytes < (size_t)workgroups * 512 * sizeof(float))
+      return fail(BSA_ERR_INVALID_ARG, "sink must hold 512 floats per workgroup");
+    Stages stages(stream);
+    const bsa_status_t st = hip_status(launch_coexec_probe(static_cast<const bf16_t*>(operands),
+                                                           mode, valu, op, acc, workgroups,
+                                                           iters, sink, stream),
+                                       "MFMA/VALU probe launch");
+    stages.done("probe_mfma_valu");
+    return st;
+  });
+}
+
 bsa_status_t bsa_probe_tile_read(const void* buf, size_t buf_bytes, int32_t tile_bytes,
                                  const int32_t* ids, size_t n_ids, int32_t waves,
                                  int32_t tiles_per_wave, uint32_t* sink, size_t sink_bytes,

@@ -60,6 +60,10 @@ hipError_t launch_validate_idx(const Geom& g, const int32_t* idx, int k_sel, int
 // listed in ids ([waves, tiles_per_wave] tile numbers of buf; sink: 64 words per wave).
 hipError_t launch_mfma_probe(const bf16_t* operands, int shape, int chains, int waves, int iters,
                              float* sink, hipStream_t s);
+// mode 0-3, valu in {0, 2, 4, 8, 16} with op 0 (fma) or {1, 2, 4} with op 1 (exp), acc 0
+// (VGPR accumulators) or 1 (AGPR accumulators); sink: 512 floats per workgroup
+hipError_t launch_coexec_probe(const bf16_t* operands, int mode, int valu, int op, int acc,
+                               int workgroups, int iters, float* sink, hipStream_t s);
 hipError_t launch_tile_read(const bf16_t* buf, size_t buf_bytes, int tile_bytes,
                             const int32_t* ids, int waves, int tiles_per_wave, uint32_t* sink,
                             hipStream_t s);

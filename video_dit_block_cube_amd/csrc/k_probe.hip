@@ -5,6 +5,9 @@
 //    1, 2, 4 or 8 independent accumulator chains per wave, operands taken from a caller buffer.  With N(0,1) bf16 operands
 //    (the data the attention products see) the chip lowers its clock under load, so this is the
 //    rate bf16 MFMA work can reach on such data; constant operands show the clock effect.
+//  * coexec_probe_kernel: bf16 MFMA and VALU work on one SIMD, either interleaved in each wave
+//    or split between the two waves that share the SIMD, against each kind alone: how much
+//    VALU work (softmax arithmetic) can run beside the products, and in which arrangement.
 //  * tile_read_kernel: every wave reads whole tiles (tile_bytes, a multiple of 1 KB) at the tile
 //    ids of its row of a caller table, as 1 KB wave-wide 16-byte-per-lane buffer loads -- the
 //    access pattern of the attention kernels' K/V and Q/dO tiles.  The caller picks the ids, and
@@ -72,6 +75,89 @@ __global__ __launch_bounds__(64) void mfma_probe_kernel(const bf16_t* __restrict
   sink[blockIdx.x * 64 + lane] = s;
 }
 
+// Eight-wave workgroups, one per CU at a time, two waves on every SIMD.  Each iteration is four products
+// (v_mfma_f32_32x32x16_bf16, four independent accumulators) and/or, after each product, V VALU
+// instructions on eight independent fp32 chains (OP 0: v_fma_f32; OP 1: v_exp_f32 of the negated
+// value, whose fixed point keeps the chain finite).  mode 0: every wave does both, the VALU
+// instructions scheduled right after each product; mode 1: on each SIMD one wave does the
+// products and the other the VALU instructions (the wave's SIMD read from the HW_ID register,
+// the first of the two in wave order taking the products); mode 2: products only; mode 3: VALU
+// only.
+// The loop of one wave: iters x 4 slots, each slot a product (DO_M) and/or V VALU instructions
+// (DO_V); with both, the VALU instructions are scheduled right after their slot's product.
+template <int V, int OP, bool DO_M, bool DO_V>
+__device__ __forceinline__ float coexec_loop(const bf16x8 a, const bf16x8 b, int lane, int iters) {
+  f32x16 acc[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[c][e] = 0.f;
+  float x[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) x[k] = 0.001f * (float)(lane + k);
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      if constexpr (DO_M) acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[c], 0, 0, 0);
+      if constexpr (DO_V) {
+#pragma unroll
+        for (int k = 0; k < V; ++k) {
+          if constexpr (OP == 0) x[k & 7] = fmaf(x[k & 7], 0.999f, 0.001f);
+          else x[k & 7] = __builtin_amdgcn_exp2f(-x[k & 7]);
+        }
+      }
+      if constexpr (DO_M && DO_V) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, V, 0);  // then V VALU instructions
+      }
+    }
+  }
+  float sum = 0.f;
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) sum += acc[c][e];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) sum += x[k];
+  return sum;
+}
+
+// Eight-wave workgroups, one per CU at a time, two waves on every SIMD.  Each iteration is four
+// products (v_mfma_f32_32x32x16_bf16, four independent accumulators) and/or, after each product,
+// V VALU instructions on eight independent fp32 chains (OP 0: v_fma_f32; OP 1: v_exp_f32 of the
+// negated value, whose fixed point keeps the chain finite).  mode 0: every wave does both;
+// mode 1: on each SIMD one wave does the products and the other the VALU instructions (the
+// wave's SIMD read from the HW_ID register, the first of the two in wave order taking the
+// products); mode 2: products only; mode 3: VALU only.
+template <int V, int OP, int ACC>
+__global__ __launch_bounds__(512) void coexec_probe_kernel(const bf16_t* __restrict__ operands,
+                                                           int mode, int iters,
+                                                           float* __restrict__ sink) {
+  // ACC 1: an (empty) use of an AGPR tells the compiler the kernel may use AGPRs, which makes it
+  // give every product an AGPR accumulator; ACC 0 leaves them in VGPRs (the kernel fits in 256)
+  if constexpr (ACC == 1) asm volatile("; agpr in use %0" ::"a"(0));
+  __shared__ int simd_of[8];
+  // 84 KB of LDS, so that one workgroup holds a CU and every SIMD runs exactly its two waves
+  __shared__ int hold[21504];
+  if (iters < 0) hold[threadIdx.x] = 0;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  // SIMD_ID is bits 5:4 of HW_ID (s_getreg_b32 hwreg(HW_REG_HW_ID, 4, 2))
+  const int simd = (int)(__builtin_amdgcn_s_getreg((1 << 11) | (4 << 6) | 4) & 3);
+  if (lane == 0) simd_of[wv] = simd;
+  __syncthreads();
+  int before = 0;  // earlier waves of this workgroup on the same SIMD
+  for (int w = 0; w < wv; ++w) before += simd_of[w] == simd ? 1 : 0;
+  const bf16x8 a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(operands + lane * 8));
+  const bf16x8 b =
+      __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(operands + (64 + lane) * 8));
+  float sum;
+  if (mode == 0) sum = coexec_loop<V, OP, true, true>(a, b, lane, iters);
+  else if (mode == 2 || (mode == 1 && before == 0)) sum = coexec_loop<V, OP, true, false>(a, b, lane, iters);
+  else sum = coexec_loop<V, OP, false, true>(a, b, lane, iters);
+  sink[blockIdx.x * 512 + threadIdx.x] = sum;
+}
+
 __global__ __launch_bounds__(64) void tile_read_kernel(const bf16_t* __restrict__ buf,
                                                        size_t buf_bytes, int tile_bytes,
                                                        const int32_t* __restrict__ ids,
@@ -117,6 +203,30 @@ hipError_t launch_mfma_probe(const bf16_t* operands, int shape, int chains, int 
     default: return hipErrorInvalidValue;
   }
 #undef BSA_PROBE
+  return hipGetLastError();
+}
+
+hipError_t launch_coexec_probe(const bf16_t* operands, int mode, int valu, int op, int acc,
+                               int workgroups, int iters, float* sink, hipStream_t s) {
+  const dim3 grid((unsigned)workgroups), block(512);
+#define BSA_COEXEC(VV, OO, AA)                                                                   \
+  hipLaunchKernelGGL((coexec_probe_kernel<VV, OO, AA>), grid, block, 0, s, operands, mode, iters, \
+                     sink)
+#define BSA_COEXEC2(VV, OO) \
+  if (acc) BSA_COEXEC(VV, OO, 1); else BSA_COEXEC(VV, OO, 0);
+  switch (op * 32 + valu) {
+    case 0: BSA_COEXEC2(0, 0); break;
+    case 2: BSA_COEXEC2(2, 0); break;
+    case 4: BSA_COEXEC2(4, 0); break;
+    case 8: BSA_COEXEC2(8, 0); break;
+    case 16: BSA_COEXEC2(16, 0); break;
+    case 33: BSA_COEXEC2(1, 1); break;
+    case 34: BSA_COEXEC2(2, 1); break;
+    case 36: BSA_COEXEC2(4, 1); break;
+    default: return hipErrorInvalidValue;
+  }
+#undef BSA_COEXEC2
+#undef BSA_COEXEC
   return hipGetLastError();
 }
 
