@@ -88,11 +88,13 @@ def test_dkdv_dispatch_order_changes_nothing(number, over):
 @pytest.mark.parametrize("number, over", [
     (5, (("heads", 4),)),                                               # D = 128: pipelined dQ
     (4, (("heads", 2), ("T", 12), ("H", 24), ("W", 40), ("cond_T", 4))),  # condition cubes
+    (5, (("heads", 2), ("H", 30), ("W", 50))),                          # ragged grid
+    (4, (("heads", 2), ("T", 12), ("H", 18), ("W", 22), ("cond_T", 4))),  # ragged, condition
 ])
 def test_dq_pipeline_changes_nothing(number, over):
-    """At head_dim 128 on grids without partial cubes dQ runs a software-pipelined loop; the plain
-    loop (BSA_TUNE_DQ_PIPELINE 0) must give the same bits, since each tile's arithmetic and the order
-    of the dQ updates are the same."""
+    """At head_dim 128 dQ runs a software-pipelined loop; the plain loop (BSA_TUNE_DQ_PIPELINE 0)
+    must give the same bits, since each tile's arithmetic (the ragged grid's clamp included) and
+    the order of the dQ updates are the same."""
     w = synth.workload(number, **dict(over))
     print_case(f"dQ pipeline {w.name} {dict(over)}")
     x = synth.make_inputs(w)

@@ -36,13 +36,16 @@ FLAGS = [
 #    its 128 copies per tile with it (with MINREG: no spills; 2.5% faster); the head_dim 64 dQ
 #    and dK/dV fit in 256 VGPRs with it (8% faster each).  The head_dim 128 dK/dV kernels already
 #    use VGPRs only and compile to the same code; the head_dim 128 one-wave dQ was 2% slower with
-#    it, so k_bwd_dq.hip does without.
+#    it, so k_bwd_dq.hip does without.  With the option, a kernel that spills computed wrong
+#    results, so it is only used where nothing spills (tests/test_build_no_spills.py): the
+#    ragged-grid pipelined dQ, which would spill, has its own file built with MINREG only.
 MINREG = ["-mllvm", "--amdgpu-sched-strategy=iterative-minreg"]
 VGPR_MFMA = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
 EXTRA_FLAGS = {
     "k_bwd_dq.hip": MINREG,
     "k_bwd_dq64.hip": VGPR_MFMA,
     "k_bwd_dq_pipe.hip": VGPR_MFMA + MINREG,
+    "k_bwd_dq_pipe_ragged.hip": MINREG,
     "k_bwd_mfma.hip": VGPR_MFMA,
 }
 

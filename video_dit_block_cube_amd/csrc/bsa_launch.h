@@ -97,8 +97,7 @@ size_t fwd_kmask_bytes(const Geom& g);
 // LDS with ds_read_b64_tr_b16).
 // k_row / v_row cover all nbk key cubes (condition cubes first), q_row / do_row the nbq query
 // cubes; dK/dV of condition key cubes go to dk_cache / dv_cache ([B, Nc, Hh, D]).
-// pipelined: at D = 128 on a grid without partial cubes, run the software-pipelined variant
-// (same bits; launch_bwd_dq_pipe).
+// pipelined: at D = 128 run the software-pipelined variant (same bits; launch_bwd_dq_pipe).
 // walk_ticks > 0 (D = 128 dK/dV and pipelined dQ only): each work item starts its walk over its
 // list at the entry nearest the phase of the 100 MHz real-time clock within that period and
 // wraps (locality experiment; the summation order then depends on timing).  0: from the start.
@@ -112,6 +111,13 @@ hipError_t launch_bwd_dq64(const Geom& g, const bf16_t* q_row, const bf16_t* do_
                            const bf16_t* k_row, const bf16_t* v_row, const float2* ld_c,
                            const int32_t* idx, int k_sel, float scale, float c_log2, int cpx,
                            float* dq, hipStream_t s);
+// k_bwd_dq_pipe_ragged.hip: the pipelined dQ at head_dim 128 on a ragged grid; called by
+// launch_bwd_dq_pipe.
+hipError_t launch_bwd_dq_pipe_ragged(const Geom& g, const bf16_t* q_row, const bf16_t* do_row,
+                                     const bf16_t* k_row, const bf16_t* v_row,
+                                     const float2* ld_c, const int32_t* idx, int k_sel,
+                                     float scale, float c_log2, int cpx, int walk_ticks,
+                                     float* dq, hipStream_t s);
 hipError_t launch_bwd_dq_pipe(const Geom& g, const bf16_t* q_row, const bf16_t* do_row,
                               const bf16_t* k_row, const bf16_t* v_row, const float2* ld_c,
                               const int32_t* idx, int k_sel, float scale, float* dq,

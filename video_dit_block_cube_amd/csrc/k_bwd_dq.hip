@@ -9,9 +9,9 @@
 //
 // This file is compiled with LLVM's register-minimising scheduler (build flags): at head_dim 128
 // it keeps the score accumulators out of the AGPRs that hold dQ^T, which trims accumulator copies
-// in the loop.  At head_dim 128 on grids whose sides are cube multiples the launcher runs the
-// software-pipelined variant (k_bwd_dq_pipe.hip) instead, which gives the same bits; head_dim 64
-// runs the instantiation in k_bwd_dq64.hip.
+// in the loop.  At head_dim 128 the launcher runs the software-pipelined variant
+// (k_bwd_dq_pipe.hip, k_bwd_dq_pipe_ragged.hip) instead, which gives the same bits, unless the
+// pipeline is switched off; head_dim 64 runs the instantiation in k_bwd_dq64.hip.
 #include "bsa_bwd_dq.h"
 
 namespace bsa {
@@ -20,7 +20,7 @@ hipError_t launch_bwd_dq_mfma(const Geom& g, const bf16_t* q_row, const bf16_t* 
                               const bf16_t* k_row, const bf16_t* v_row, const float2* ld_c,
                               const int32_t* idx, int k_sel, float scale, float* dq,
                               bool pipelined, int walk_ticks, hipStream_t s) {
-  if (pipelined && g.D == 128 && !g.ragged)
+  if (pipelined && g.D == 128)
     return launch_bwd_dq_pipe(g, q_row, do_row, k_row, v_row, ld_c, idx, k_sel, scale, dq,
                               walk_ticks, s);
   const int cpx = (g.nbq + 7) / 8;
