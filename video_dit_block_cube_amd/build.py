@@ -32,7 +32,7 @@ FLAGS = [
 #    score accumulators out of the AGPRs that hold dQ^T (about 2-3% faster).
 #  * VGPR_MFMA, every MFMA writing architectural VGPRs.  Without it the compiler gives every MFMA
 #    an AGPR destination once a kernel may use more than 256 registers, and each score element
-#    then costs a v_accvgpr_read before its exponential.  The pipelined dQ (512 registers) loses
+#    then costs a v_accvgpr_read before its exponential.  The pipelined dQ (about 490 registers) loses
 #    its 128 copies per tile with it (with MINREG: no spills; 2.5% faster); the head_dim 64 dQ
 #    and dK/dV fit in 256 VGPRs with it (8% faster each).  The head_dim 128 dK/dV kernels already
 #    use VGPRs only and compile to the same code; the head_dim 128 one-wave dQ was 2% slower with
