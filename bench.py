@@ -88,10 +88,26 @@ def stage_bytes(name: str, p, k_sel: int) -> float | None:
             "bwd_prep": 3 * tensor + 3 * per_query + 2 * idx}.get(name)
 
 
+def kernel_build_flags(name: str) -> str:
+    """The hipcc options build.py compiles csrc/<name> with, include paths left out."""
+    from video_dit_block_cube_amd import build as B
+    flags, skip = [], False
+    for f in B.FLAGS:
+        if skip:
+            skip = False
+            continue
+        if f == "-I":
+            skip = True
+            continue
+        flags.append(f)
+    return " ".join(flags + list(B.EXTRA_FLAGS.get(name, [])))
+
+
 def profile_record(stage: str) -> dict:
     """Counter results of a kernel (profiles/traffic_<stage>.txt: bytes fetched from beyond L2
     plus bytes written, per launch, from FETCH_SIZE and WRITE_SIZE scaled by a plain copy; shader
-    clock), or {} when no measurement exists or the kernel source changed since it was taken.
+    clock), or {} when no measurement exists or the kernel source or its build options changed
+    since it was taken.
     FETCH_SIZE counts every byte the L2 fetches, Infinity Cache hits included, so these bytes
     bound HBM traffic from above."""
     path = os.path.join(ROOT, "profiles", f"traffic_{stage}.txt")
@@ -110,6 +126,10 @@ def profile_record(stage: str) -> dict:
     for f in srcs:
         h.update(open(f, "rb").read())
     if h.hexdigest() != kv.get("source_sha256"):
+        return {}
+    # "build_flags": the compiler options the kernel's file is built with (build.py, include
+    # paths left out); a record taken under other options is not this kernel's
+    if "build_flags" in kv and kv["build_flags"] != kernel_build_flags(kv.get("build_file", "")):
         return {}
     rec = {}
     for key in ("beyond_l2_bytes_per_launch", "clock_ghz"):
